@@ -1,0 +1,145 @@
+"""Seeded synthetic inputs for the routed-expert epilogue.
+
+This module is shared by the tests, the smoke check and the benchmark. It
+holds none of the method's arithmetic: only random draws, their placement and
+their rounding to the input dtypes (bfloat16 via torch's round-to-nearest-even
+conversion, fp32 for probabilities). It imports nothing else from this package
+and nothing from the oracle.
+
+The five named workloads follow the shapes and value distributions of the
+pages' workload ("the 16-node shape" in the nemo_automodel.components.moe
+.swiglu_triton module description, whose per-GPU share gives x of about
+1.1 GB) and of the router-weight multiply (nemo_automodel.components.moe
+.optimized_ops, x [tokens, hidden]):
+
+  swiglu_256x128      L=7,  x ~ N(0, 3^2), 5% of x entries exactly +-7
+  swiglu_8192x2048    L=10, x ~ N(0, 4^2), probs renormalised per 8 rows (top-8)
+  swiglu_131072x2048  L=10, x ~ N(0, 4^2)            (x is 131072 x 4096 bf16)
+  swiglu_100003x1536  L=7,  x ~ N(0, 5^2), 10% of x entries in {-7, +7, 0},
+                      20% of rows with probability exactly 0
+  router_65536x7168   x ~ N(0, 1)
+
+probs ~ U(0, 1) fp32 unless stated, grad_out ~ N(0, 1) bf16 everywhere.
+
+Readings taken where the workload text is loose:
+  - "p% of entries" is read per entry: each entry is special independently
+    with probability p (Bernoulli), and the special value is drawn uniformly
+    from the listed set;
+  - U(0, 1) is numpy's float32 random() in [0, 1);
+  - top-8 renormalisation divides each group of 8 consecutive rows by the
+    group's sum, computed in float64 and rounded once to float32;
+  - normals are drawn in float32, scaled by sigma in float32 and rounded to
+    bfloat16 to nearest-even.
+Draws are made in fixed chunks of rows from independent streams spawned from
+numpy.random.SeedSequence(seed), so a workload is the same on every machine.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+CHUNK_ROWS = 4096
+
+
+def _to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), rounded to nearest-even by torch."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    op: str                   # "swiglu" or "router"
+    rows: int
+    cols: int                 # inter (swiglu) or hidden (router)
+    limit: float | None       # L for swiglu, None for router
+    x_sigma: float
+    seed: int
+    x_special_frac: float = 0.0
+    x_special_values: tuple = ()
+    probs_kind: str = "uniform"   # "uniform" | "top8" | "uniform_zeros"
+    probs_zero_frac: float = 0.0
+    notes: str = field(default="", compare=False)
+
+    @property
+    def x_cols(self) -> int:
+        return 2 * self.cols if self.op == "swiglu" else self.cols
+
+    def fwd_bytes(self) -> int:
+        """Algorithmic HBM bytes of one forward pass (every input read once,
+        every output written once)."""
+        if self.op == "swiglu":
+            return self.rows * (6 * self.cols + 4)
+        return self.rows * (4 * self.cols + 4)
+
+    def bwd_bytes(self, with_grad_probs: bool = True) -> int:
+        """Algorithmic HBM bytes of one backward pass."""
+        if self.op == "swiglu":
+            return self.rows * (10 * self.cols + 4 + (4 if with_grad_probs else 0))
+        if with_grad_probs:
+            return self.rows * (6 * self.cols + 8)
+        return self.rows * (4 * self.cols + 4)
+
+    def generate(self, rows: int | None = None) -> dict:
+        """Inputs as numpy arrays: x (uint16 bf16 bits [rows, x_cols]),
+        probs (float32 [rows]), grad_out (uint16 bf16 bits [rows, cols]).
+
+        rows < self.rows gives the leading rows of the same workload (the same
+        values as the full draw, for the chunks it covers)."""
+        n = self.rows if rows is None else int(rows)
+        if n < 0 or n > self.rows:
+            raise ValueError("rows out of range")
+        ss = np.random.SeedSequence(self.seed)
+        s_x, s_xmask, s_p, s_pmask, s_gy = [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(5)]
+        xc, gc = self.x_cols, self.cols
+        x = np.empty((n, xc), dtype=np.uint16)
+        gy = np.empty((n, gc), dtype=np.uint16)
+        special = np.array(self.x_special_values, dtype=np.float32)
+        for r0 in range(0, n, CHUNK_ROWS):
+            m = min(CHUNK_ROWS, n - r0)
+            xf = s_x.standard_normal((m, xc), dtype=np.float32)
+            xf *= np.float32(self.x_sigma)
+            if self.x_special_frac > 0.0:
+                hit = s_xmask.random((m, xc), dtype=np.float32) < np.float32(self.x_special_frac)
+                pick = s_xmask.integers(0, len(special), size=int(hit.sum()))
+                xf[hit] = special[pick]
+            x[r0:r0 + m] = _to_bf16_bits(xf)
+            gy[r0:r0 + m] = _to_bf16_bits(s_gy.standard_normal((m, gc), dtype=np.float32))
+        probs = s_p.random(self.rows, dtype=np.float32)[:n].copy()
+        if self.probs_kind == "top8":
+            p64 = probs.astype(np.float64)
+            for g0 in range(0, n, 8):
+                p64[g0:g0 + 8] /= p64[g0:g0 + 8].sum()
+            probs = p64.astype(np.float32)
+        elif self.probs_kind == "uniform_zeros":
+            zero = s_pmask.random(self.rows, dtype=np.float32)[:n] < np.float32(self.probs_zero_frac)
+            probs[zero] = np.float32(0.0)
+        elif self.probs_kind != "uniform":
+            raise ValueError(self.probs_kind)
+        return {"x": x, "probs": probs, "grad_out": gy}
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("swiglu_256x128", "swiglu", 256, 128, 7.0, 3.0, seed=1,
+                 x_special_frac=0.05, x_special_values=(-7.0, 7.0)),
+        Workload("swiglu_8192x2048", "swiglu", 8192, 2048, 10.0, 4.0, seed=2, probs_kind="top8"),
+        Workload("swiglu_131072x2048", "swiglu", 131072, 2048, 10.0, 4.0, seed=3),
+        Workload("swiglu_100003x1536", "swiglu", 100003, 1536, 7.0, 5.0, seed=4,
+                 x_special_frac=0.10, x_special_values=(-7.0, 7.0, 0.0),
+                 probs_kind="uniform_zeros", probs_zero_frac=0.20),
+        Workload("router_65536x7168", "router", 65536, 7168, None, 1.0, seed=5),
+    ]
+}
+
+# The benchmark's headline workload: the per-GPU share of the large-node shape.
+HEADLINE = "swiglu_131072x2048"
+
+
+def custom(op: str, rows: int, cols: int, limit: float | None = None, x_sigma: float = 4.0,
+           seed: int = 0, **kw) -> Workload:
+    """An ad-hoc workload (test shapes: ragged tails, tiny rows, odd widths)."""
+    return Workload(f"{op}_{rows}x{cols}_s{seed}", op, rows, cols, limit, x_sigma, seed=seed, **kw)

@@ -1,0 +1,151 @@
+"""CPU oracle for the routed-expert epilogue (ctypes wrapper of liboracle.so).
+
+TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package. The product path (the HIP library
+and its Python binding) never imports or calls it, and the two share no code.
+
+All arrays are numpy: bfloat16 tensors travel as uint16 bit patterns, probs and
+probability gradients as float32. See oracle.c for the definitions and the
+passages of the pages each function follows.
+
+Parity status: every function here is pinned by tests/test_oracle_pins.py
+(library cross-checks, exhaustive bfloat16 sweeps, finite differences, exact
+sums, hand-derived cases); none is "parity unpinned".
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_i64 = ctypes.c_int64
+
+
+def default_threads() -> int:
+    """Threads the oracle uses unless told otherwise (host cores, at most 16)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build  # build only if nothing is built
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f32.restype = ctypes.c_float
+    lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_swiglu_point.argtypes = [ctypes.c_float] * 5 + [_f32p]
+    lib.oracle_swiglu_point.restype = None
+    lib.oracle_swiglu_clamped_fwd.argtypes = [_u16p, _f32p, _u16p, _i64, _i64, ctypes.c_float, ctypes.c_int]
+    lib.oracle_swiglu_clamped_fwd.restype = None
+    lib.oracle_swiglu_clamped_bwd.argtypes = [_u16p, _f32p, _u16p, _u16p, _f32p, _i64, _i64,
+                                              ctypes.c_float, ctypes.c_int]
+    lib.oracle_swiglu_clamped_bwd.restype = None
+    lib.oracle_router_weight_mul_fwd.argtypes = [_u16p, _f32p, _u16p, _i64, _i64, ctypes.c_int]
+    lib.oracle_router_weight_mul_fwd.restype = None
+    lib.oracle_router_weight_mul_bwd.argtypes = [_u16p, _u16p, _f32p, _u16p, _f32p, _i64, _i64, ctypes.c_int]
+    lib.oracle_router_weight_mul_bwd.restype = None
+    _lib = lib
+    return lib
+
+
+def _arr(a, dtype, shape):
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    if a.size != int(np.prod(shape)):
+        raise ValueError(f"expected {shape} elements, got shape {a.shape}")
+    return a
+
+
+def _p(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype)) if a is not None else None
+
+
+# ---- scalar helpers (used by the pin tests) ------------------------------
+
+def bf16_to_f32(b: int) -> float:
+    return float(_load().oracle_bf16_to_f32(int(b)))
+
+
+def f32_to_bf16(f: float) -> int:
+    return int(_load().oracle_f32_to_bf16(float(f)))
+
+
+def swiglu_point(g: float, u: float, p: float, gy: float, L: float):
+    """(y_f32, d_gate_f32, d_up_f32, dprob_term_f32) for one element, unrounded."""
+    out = (ctypes.c_float * 4)()
+    _load().oracle_swiglu_point(g, u, p, gy, L, out)
+    return tuple(float(v) for v in out)
+
+
+def f32_to_bf16_array(a):
+    """Vector form of f32_to_bf16 (loops in Python over ctypes: small inputs only)."""
+    lib = _load()
+    flat = np.ascontiguousarray(a, dtype=np.float32).ravel()
+    return np.array([lib.oracle_f32_to_bf16(float(v)) for v in flat], dtype=np.uint16).reshape(np.shape(a))
+
+
+# ---- tensor entry points --------------------------------------------------
+
+def swiglu_clamped_fwd(x, probs, rows, inter, L, threads=None):
+    """y (uint16 [rows, inter]) = bf16(silu(min(gate, L)) * clamp(up, -L, L) * p)."""
+    x = _arr(x, np.uint16, (rows, 2 * inter))
+    probs = _arr(probs, np.float32, (rows,))
+    y = np.empty((rows, inter), dtype=np.uint16)
+    _load().oracle_swiglu_clamped_fwd(_p(x, ctypes.c_uint16), _p(probs, ctypes.c_float),
+                                      _p(y, ctypes.c_uint16), rows, inter, float(L),
+                                      threads or default_threads())
+    return y
+
+
+def swiglu_clamped_bwd(x, probs, grad_y, rows, inter, L, want_grad_probs=True, threads=None):
+    """(grad_x uint16 [rows, 2*inter], grad_probs float32 [rows] or None)."""
+    x = _arr(x, np.uint16, (rows, 2 * inter))
+    probs = _arr(probs, np.float32, (rows,))
+    grad_y = _arr(grad_y, np.uint16, (rows, inter))
+    grad_x = np.empty((rows, 2 * inter), dtype=np.uint16)
+    grad_probs = np.empty((rows,), dtype=np.float32) if want_grad_probs else None
+    _load().oracle_swiglu_clamped_bwd(_p(x, ctypes.c_uint16), _p(probs, ctypes.c_float),
+                                      _p(grad_y, ctypes.c_uint16), _p(grad_x, ctypes.c_uint16),
+                                      _p(grad_probs, ctypes.c_float), rows, inter, float(L),
+                                      threads or default_threads())
+    return grad_x, grad_probs
+
+
+def router_weight_mul_fwd(x, probs, rows, hidden, threads=None):
+    """out (uint16 [rows, hidden]) = bf16(fp32(x) * p)."""
+    x = _arr(x, np.uint16, (rows, hidden))
+    probs = _arr(probs, np.float32, (rows,))
+    out = np.empty((rows, hidden), dtype=np.uint16)
+    _load().oracle_router_weight_mul_fwd(_p(x, ctypes.c_uint16), _p(probs, ctypes.c_float),
+                                         _p(out, ctypes.c_uint16), rows, hidden,
+                                         threads or default_threads())
+    return out
+
+
+def router_weight_mul_bwd(grad_out, x, probs, rows, hidden, want_grad_probs=True, threads=None):
+    """(grad_x uint16 [rows, hidden], grad_probs float32 [rows] or None); x may be None
+    when want_grad_probs is False."""
+    grad_out = _arr(grad_out, np.uint16, (rows, hidden))
+    if want_grad_probs:
+        x = _arr(x, np.uint16, (rows, hidden))
+    else:
+        x = None
+    probs = _arr(probs, np.float32, (rows,))
+    grad_x = np.empty((rows, hidden), dtype=np.uint16)
+    grad_probs = np.empty((rows,), dtype=np.float32) if want_grad_probs else None
+    _load().oracle_router_weight_mul_bwd(_p(grad_out, ctypes.c_uint16), _p(x, ctypes.c_uint16),
+                                         _p(probs, ctypes.c_float), _p(grad_x, ctypes.c_uint16),
+                                         _p(grad_probs, ctypes.c_float), rows, hidden,
+                                         threads or default_threads())
+    return grad_x, grad_probs

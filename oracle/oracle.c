@@ -1,0 +1,196 @@
+/*
+ * CPU oracle for the routed-expert epilogue: clamped SwiGLU times routing
+ * probability (forward and backward) and the fp32 router-weight multiply
+ * (forward and backward).
+ *
+ * TEST INFRASTRUCTURE ONLY. The product library never includes, links, loads
+ * or calls this file; only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg use it. It shares no code, header, helper or
+ * table with the HIP library.
+ *
+ * How it computes (plain and slow on purpose):
+ *   - one element at a time, in the order the definitions write the
+ *     expression, in IEEE binary32 with one rounding per operation (built
+ *     with -ffp-contract=off and without fast-math, so no fused
+ *     multiply-add and no reassociation);
+ *   - exp is the host C library's expf; division is the IEEE division;
+ *   - per-row probability gradients: binary32 terms summed in binary64 in
+ *     ascending column order, rounded once to binary32;
+ *   - every bfloat16 result is rounded once from binary32, to nearest, ties
+ *     to even.
+ * Rows are independent, so rows may be handed to several OpenMP threads;
+ * that changes no result.
+ *
+ * Sources (the pages' own words are restated, not quoted):
+ *   [SW] nemo_automodel.components.moe.swiglu_triton, module description:
+ *        y = silu(clamp(gate, max=L)) * clamp(up, -L, L) * probs on the
+ *        grouped-GEMM output x = [gate | up] (bf16, [rows, 2*inter]) with
+ *        fp32 probs [rows, 1]; fp32 math with the result rounded to x's
+ *        dtype; the backward writes d_gate / d_up into the two halves of
+ *        grad_x and reduces one probability gradient per row; clamp
+ *        gradients follow torch.clamp, i.e. inclusive range masks taken on
+ *        the input values.
+ *   [RW] nemo_automodel.components.moe.optimized_ops,
+ *        _RouterWeightMulFunction class description and the _rw_fwd_core,
+ *        _rw_bwd_x_core and _rw_bwd_probs_core entries: out = (x * probs)
+ *        in fp32 cast to the output dtype; grad_x = (grad_out * probs) in
+ *        fp32 cast to x's dtype; grad_probs = (grad_out * x).sum(-1) in fp32
+ *        cast to probs' dtype.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ---- bfloat16 <-> binary32 ------------------------------------------- */
+
+/* Widening is exact: a bfloat16 is the upper half of a binary32. */
+float oracle_bf16_to_f32(uint16_t b)
+{
+    uint32_t bits = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+/* Round a binary32 to bfloat16, to nearest, ties to even (the rounding of
+ * torch's .to(torch.bfloat16)). The kept part is the upper 16 bits; the
+ * dropped lower 16 bits decide: above half -> round up, exactly half ->
+ * round up only if the kept part is odd, below half -> truncate. Rounding up
+ * may carry into the exponent, which is the correct result (up to +-inf).
+ * NaN stays NaN: its sign and top payload bits are kept and the quiet bit
+ * is set. */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    uint32_t kept = bits >> 16;
+    uint32_t dropped = bits & 0xFFFFu;
+    if ((bits & 0x7F800000u) == 0x7F800000u && (bits & 0x007FFFFFu) != 0)
+        return (uint16_t)(kept | 0x0040u);
+    if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))
+        kept += 1u;
+    return (uint16_t)kept;
+}
+
+/* ---- clamped SwiGLU x probs: one element ------------------------------ */
+
+/*
+ * [SW] All quantities for one element (gate g, up u, probability p, upstream
+ * gradient gy, limit L), in binary32:
+ *   out[0] = y before rounding        = (silu(gc) * uc) * p
+ *   out[1] = d_gate before rounding   = mask_g ? (gy*p * uc) * silu'(gc) : +0
+ *   out[2] = d_up before rounding     = mask_u ? (gy*p) * silu(gc)      : +0
+ *   out[3] = this element's term of the probability gradient = gy * (silu(gc)*uc)
+ * with gc = min(g, L) (upper clamp only), uc = clamp(u, -L, L),
+ * silu(z) = z * sigma(z), sigma(z) = 1 / (1 + exp(-z)),
+ * silu'(z) = sigma(z) * (1 + z * (1 - sigma(z))),
+ * mask_g = (g <= L), mask_u = (-L <= u <= L): the inclusive torch.clamp
+ * masks on the input values. A clamp passes NaN through (a comparison with
+ * NaN is false), and a NaN input fails its mask, as torch.clamp does.
+ * Masked gradients are written as +0 (a selection, not a product with the
+ * mask).
+ */
+void oracle_swiglu_point(float g, float u, float p, float gy, float L, float out[4])
+{
+    float gc = (g > L) ? L : g;
+    float uc = (u > L) ? L : ((u < -L) ? -L : u);
+    float sig = 1.0f / (1.0f + expf(-gc));
+    float a = gc * sig;                 /* silu(gc) */
+    float h = a * uc;
+    float t = gy * p;
+    float dsilu = sig * (1.0f + gc * (1.0f - sig));
+    int mask_g = (g <= L);
+    int mask_u = (-L <= u) && (u <= L);
+    out[0] = h * p;
+    out[1] = mask_g ? (t * uc) * dsilu : 0.0f;
+    out[2] = mask_u ? t * a : 0.0f;
+    out[3] = gy * h;
+}
+
+/* ---- clamped SwiGLU x probs: whole tensors ---------------------------- */
+
+/* [SW] forward. x is [rows, 2*inter] row-major (gate = columns [0, inter),
+ * up = columns [inter, 2*inter)); probs is [rows]; y is [rows, inter]. */
+void oracle_swiglu_clamped_fwd(const uint16_t *x, const float *probs, uint16_t *y,
+                               int64_t rows, int64_t inter, float L, int nthreads)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (r = 0; r < rows; ++r) {
+        const uint16_t *xr = x + r * 2 * inter;
+        for (int64_t j = 0; j < inter; ++j) {
+            float q[4];
+            oracle_swiglu_point(oracle_bf16_to_f32(xr[j]), oracle_bf16_to_f32(xr[inter + j]),
+                                probs[r], 0.0f, L, q);
+            y[r * inter + j] = oracle_f32_to_bf16(q[0]);
+        }
+    }
+}
+
+/* [SW] backward. grad_y is [rows, inter]; grad_x is [rows, 2*inter] with
+ * d_gate in the first half of each row and d_up in the second; grad_probs is
+ * [rows] and may be NULL, in which case no probability gradient is formed. */
+void oracle_swiglu_clamped_bwd(const uint16_t *x, const float *probs, const uint16_t *grad_y,
+                               uint16_t *grad_x, float *grad_probs,
+                               int64_t rows, int64_t inter, float L, int nthreads)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (r = 0; r < rows; ++r) {
+        const uint16_t *xr = x + r * 2 * inter;
+        const uint16_t *gyr = grad_y + r * inter;
+        uint16_t *gxr = grad_x + r * 2 * inter;
+        double acc = 0.0;
+        for (int64_t j = 0; j < inter; ++j) {
+            float q[4];
+            oracle_swiglu_point(oracle_bf16_to_f32(xr[j]), oracle_bf16_to_f32(xr[inter + j]),
+                                probs[r], oracle_bf16_to_f32(gyr[j]), L, q);
+            gxr[j] = oracle_f32_to_bf16(q[1]);
+            gxr[inter + j] = oracle_f32_to_bf16(q[2]);
+            acc += (double)q[3];
+        }
+        if (grad_probs)
+            grad_probs[r] = (float)acc;
+    }
+}
+
+/* ---- fp32 router-weight multiply -------------------------------------- */
+
+/* [RW] _rw_fwd_core: out = bf16(fp32(x) * p). x and out are [rows, hidden];
+ * probs is [rows]. */
+void oracle_router_weight_mul_fwd(const uint16_t *x, const float *probs, uint16_t *out,
+                                  int64_t rows, int64_t hidden, int nthreads)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (r = 0; r < rows; ++r) {
+        for (int64_t k = 0; k < hidden; ++k) {
+            float v = oracle_bf16_to_f32(x[r * hidden + k]) * probs[r];
+            out[r * hidden + k] = oracle_f32_to_bf16(v);
+        }
+    }
+}
+
+/* [RW] _rw_bwd_x_core and _rw_bwd_probs_core:
+ *   grad_x[r,k]   = bf16(fp32(grad_out[r,k]) * p[r])
+ *   grad_probs[r] = sum_k fp32(grad_out[r,k]) * fp32(x[r,k])
+ * grad_probs may be NULL (probabilities that carry no gradient); x is then
+ * not read and may be NULL too. */
+void oracle_router_weight_mul_bwd(const uint16_t *grad_out, const uint16_t *x, const float *probs,
+                                  uint16_t *grad_x, float *grad_probs,
+                                  int64_t rows, int64_t hidden, int nthreads)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (r = 0; r < rows; ++r) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < hidden; ++k) {
+            float g = oracle_bf16_to_f32(grad_out[r * hidden + k]);
+            grad_x[r * hidden + k] = oracle_f32_to_bf16(g * probs[r]);
+            if (grad_probs)
+                acc += (double)(g * oracle_bf16_to_f32(x[r * hidden + k]));
+        }
+        if (grad_probs)
+            grad_probs[r] = (float)acc;
+    }
+}
