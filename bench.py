@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert epilogue on one MI355X.
+
+A step is one pass of the whole path over the workload, inputs resident in
+HBM: swiglu_clamped_fwd followed by swiglu_clamped_bwd (with the per-row
+probability gradient), launched through the C ABI on torch's current stream.
+The default workload is the per-GPU share of the pages' large-node shape:
+rows = 131072, inter = 2048 (x is 131072 x 4096 bf16, about 1.07 GB), L = 10.
+
+value = algorithmic bytes of one step / wall time of one step, where the
+algorithmic bytes are every input read once and every output written once:
+  forward  rows * (6*inter + 4)     (x, probs in; y out)
+  backward rows * (10*inter + 8)    (x, grad_y, probs in; grad_x, grad_probs out)
+Per-kernel times come from HIP events recorded on the launch stream around
+every launch inside the timed region.
+
+Prints one JSON line. Options:
+  --gpus N           only 1 is measured (the path has no cross-GPU step here)
+  --steps K          timed steps (default 100)
+  --warmup W         untimed steps first (default 10)
+  --workload NAME    swiglu_* or router_65536x7168 (router: fwd + bwd of the
+                     fp32 router-weight multiply)
+  --no-cpu-baseline  skip the oracle timing on the host
+  --copy-calibration time torch's device copy of 1 GiB instead (the plain copy
+                     kernel whose counter readings scale FETCH_SIZE/WRITE_SIZE)
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published peak
+METRICS = {
+    "swiglu": "achieved HBM GB/s (% of MI355X peak), clamped-SwiGLU fwd+bwd at 131072×4096 bf16",
+    "router": "achieved HBM GB/s (% of MI355X peak), fp32 router-weight multiply fwd+bwd",
+}
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=None)
+    ap.add_argument("--copy-calibration", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    """Digest of the HIP sources and build flags, to tell whether counter
+    readings taken earlier still describe the kernels being timed."""
+    from moe_routed_expert_amd import build as hip_build
+    h = hashlib.sha256()
+    for path in hip_build.sources() + [os.path.join(hip_build.CSRC, "epi_common.h"),
+                                       os.path.join(ROOT, "include", "moe_epi.h")]:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    h.update(" ".join(hip_build.FLAGS).encode())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+    (scaled by the copy-kernel calibration), if taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(args):
+    import torch
+    n = 1 << 29  # 2**29 bf16 = 1 GiB
+    src = torch.randn(n, device="cuda").to(torch.bfloat16)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    avg = sum(ms) / len(ms)
+    nbytes = 2 * n * 2
+    print(json.dumps({"calibration": "torch device copy", "bytes_read_per_launch": n * 2,
+                      "bytes_written_per_launch": n * 2, "avg_ms": avg, "median_ms": ms[len(ms) // 2],
+                      "GB/s": nbytes / (avg * 1e-3) / 1e9}), flush=True)
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}). "
+              "Rows are independent and every reduction stays inside a row, so the path shards by rows "
+              "with no exchange; per-GPU throughput is the figure. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_routed_expert_amd as epi
+    from moe_routed_expert_amd.workloads import HEADLINE, WORKLOADS
+
+    if not os.path.exists(epi.binding.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    epi.binding.lib()
+    if args.copy_calibration:
+        return copy_calibration(args)
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    d = w.generate()
+    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    p = torch.from_numpy(d["probs"]).to(dev)
+    gy = torch.from_numpy(d["grad_out"].view(np.int16)).view(torch.bfloat16).to(dev)
+    rows, cols = w.rows, w.cols
+    if w.op == "swiglu":
+        y = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+        gx = torch.empty_like(x)
+        gp = torch.empty((rows,), dtype=torch.float32, device=dev)
+        names = ("swiglu_clamped_fwd", "swiglu_clamped_bwd")
+        fwd = lambda: epi.swiglu_clamped_fwd(x, p, y, w.limit)
+        bwd = lambda: epi.swiglu_clamped_bwd(x, p, gy, gx, gp, w.limit)
+    else:
+        out = torch.empty_like(x)
+        gx = torch.empty_like(x)
+        gp = torch.empty((rows,), dtype=torch.float32, device=dev)
+        names = ("router_weight_mul_fwd", "router_weight_mul_bwd")
+        fwd = lambda: epi.router_weight_mul_fwd(x, p, out)
+        bwd = lambda: epi.router_weight_mul_bwd(gy, x, p, gx, gp)
+    fwd_b, bwd_b = w.fwd_bytes(), w.bwd_bytes()
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [(E(), E(), E()) for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in evs:
+        e0.record()
+        fwd()
+        e1.record()
+        bwd()
+        e2.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = np.array([a.elapsed_time(b) for a, b, _ in evs])
+    bwd_ms = np.array([b.elapsed_time(c) for _, b, c in evs])
+
+    ms_per_step = wall * 1e3 / args.steps
+    value = (fwd_b + bwd_b) / (ms_per_step * 1e-3) / 1e9
+
+    def kstats(name, nbytes, ms):
+        avg = float(ms.mean())
+        gbs = nbytes / (avg * 1e-3) / 1e9
+        return {"avg_us": avg * 1e3, "median_us": float(np.median(ms)) * 1e3, "min_us": float(ms.min()) * 1e3,
+                "algorithmic_bytes": nbytes, "GB/s": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS}
+
+    kernels = {names[0]: kstats(names[0], fwd_b, fwd_ms), names[1]: kstats(names[1], bwd_b, bwd_ms)}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    traffic = load_traffic(dom, w.name)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GB/s"], "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": kernels[dom]["GB/s"] / PEAK_HBM_GBS, "traffic": traffic,
+                "algorithmic_bytes_per_launch": kernels[dom]["algorithmic_bytes"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = args.cpu_threads or oracle.default_threads()
+        print(f"[bench] oracle on the host ({threads} threads), whole workload", file=sys.stderr, flush=True)
+        t = time.perf_counter()
+        if w.op == "swiglu":
+            oracle.swiglu_clamped_fwd(d["x"], d["probs"], rows, cols, w.limit, threads=threads)
+            oracle.swiglu_clamped_bwd(d["x"], d["probs"], d["grad_out"], rows, cols, w.limit, threads=threads)
+        else:
+            oracle.router_weight_mul_fwd(d["x"], d["probs"], rows, cols, threads=threads)
+            oracle.router_weight_mul_bwd(d["grad_out"], d["x"], d["probs"], rows, cols, threads=threads)
+        ct = time.perf_counter() - t
+        cpu = {"value": (fwd_b + bwd_b) / ct / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"the whole workload ({rows} rows), forward + backward once, {ct:.2f} s"}
+
+    line = {
+        "metric": METRICS[w.op] if w.name == HEADLINE or w.op == "router" else METRICS["swiglu"] + f" ({w.name})",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": w.op, "rows": rows,
+                   ("inter" if w.op == "swiglu" else "hidden"): cols,
+                   "limit": w.limit, "io": "bf16 tensors, fp32 probs; fp32 arithmetic",
+                   "bytes_per_step": fwd_b + bwd_b},
+        "frac_of_peak": value / PEAK_HBM_GBS,
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

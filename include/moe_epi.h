@@ -1,0 +1,129 @@
+/*
+ * libmoe_epi — routed-expert epilogue kernels for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Callers need no HIP headers: bfloat16 tensors are passed as uint16_t
+ * bit patterns, streams as void* (a hipStream_t; NULL selects the default
+ * stream).
+ *
+ * Common contract of every compute entry point below:
+ *   Memory    All tensor pointers are device-accessible memory allocated and
+ *             owned by the caller; the library allocates nothing, keeps no
+ *             state between calls and never synchronises. Layouts are dense
+ *             row-major with no padding: one probability per row
+ *             ([rows] == [rows, 1]). The call only validates its arguments and
+ *             queues the kernel on `stream`; results are ready when the stream
+ *             reaches that point. Calls are thread-safe.
+ *   Dtypes    x, y, gradients of x/y: bfloat16. probs, grad_probs: float32.
+ *             All arithmetic is float32; each bfloat16 result is rounded once,
+ *             to nearest with ties to even.
+ *   Errors    Arguments are checked on the host before any HIP call. On a bad
+ *             argument the call returns a nonzero moe_epi_status, launches
+ *             nothing and leaves every output untouched. rows == 0 is valid
+ *             and launches nothing. A failure reported by the HIP runtime at
+ *             launch returns MOE_EPI_ERR_LAUNCH.
+ *   Alignment bfloat16 pointers must be 2-byte aligned and float32 pointers
+ *             4-byte aligned. When every bfloat16 pointer is 16-byte aligned
+ *             and the row width (inter or hidden) is a multiple of 8, the
+ *             kernels move 16 bytes per lane per access; otherwise a
+ *             per-element path runs (same results, lower bandwidth).
+ *   Aliasing  No output may overlap any input or another output.
+ */
+#ifndef MOE_EPI_H
+#define MOE_EPI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_epi_status {
+    MOE_EPI_SUCCESS = 0,
+    MOE_EPI_ERR_NULL_POINTER = 1, /* a required pointer is NULL                              */
+    MOE_EPI_ERR_BAD_SHAPE = 2,    /* rows < 0, inter/hidden <= 0, or a byte size overflows   */
+    MOE_EPI_ERR_BAD_LIMIT = 3,    /* limit is not finite or not > 0                          */
+    MOE_EPI_ERR_ALIAS = 4,        /* an output overlaps an input or another output           */
+    MOE_EPI_ERR_MISALIGNED = 5,   /* a pointer is not aligned to its element size            */
+    MOE_EPI_ERR_LAUNCH = 6        /* the HIP runtime reported an error at kernel launch      */
+} moe_epi_status;
+
+/*
+ * Clamped SwiGLU times routing probability, forward.
+ * Defined on the page "nemo_automodel.components.moe.swiglu_triton", module
+ * description (the DeepSeek-V4-style activation used when swiglu_limit > 0):
+ *   for r < rows, j < inter, with gate = x[r, j], up = x[r, inter + j], p = probs[r]:
+ *     y[r, j] = bf16( silu(min(gate, limit)) * clamp(up, -limit, limit) * p )
+ *   silu(z) = z / (1 + exp(-z)); math in float32, one rounding to bfloat16.
+ *   The gate is clamped from above only; a NaN input propagates to y.
+ *   x     [rows, 2*inter] bf16 (gate half, then up half, in each row)   in
+ *   probs [rows] float32                                                in
+ *   y     [rows, inter] bf16                                            out
+ *   limit finite, > 0.
+ * Returns a moe_epi_status.
+ */
+int swiglu_clamped_fwd(const uint16_t *x, const float *probs, uint16_t *y,
+                       int64_t rows, int64_t inter, float limit, void *stream);
+
+/*
+ * Clamped SwiGLU times routing probability, single-pass backward.
+ * Defined on the page "nemo_automodel.components.moe.swiglu_triton", module
+ * description: one pass writes d_gate and d_up into the two halves of grad_x
+ * and reduces the per-row probability gradient; clamp gradients follow
+ * torch.clamp, i.e. inclusive masks on the input values:
+ *   gc = min(gate, limit), uc = clamp(up, -limit, limit), s = sigmoid(gc),
+ *   t = grad_y[r, j] * p,
+ *   grad_x[r, j]         = bf16( gate <= limit          ? (t * uc) * s * (1 + gc * (1 - s)) : +0 )
+ *   grad_x[r, inter + j] = bf16( -limit <= up <= limit  ? t * gc * s                        : +0 )
+ *   grad_probs[r]        = sum_j grad_y[r, j] * (gc * s * uc)     (float32, any summation order)
+ *   x          [rows, 2*inter] bf16     in
+ *   probs      [rows] float32           in
+ *   grad_y     [rows, inter] bf16       in
+ *   grad_x     [rows, 2*inter] bf16     out
+ *   grad_probs [rows] float32           out; may be NULL (probabilities that carry no
+ *                                       gradient), then it is neither formed nor written.
+ * Returns a moe_epi_status.
+ */
+int swiglu_clamped_bwd(const uint16_t *x, const float *probs, const uint16_t *grad_y,
+                       uint16_t *grad_x, float *grad_probs,
+                       int64_t rows, int64_t inter, float limit, void *stream);
+
+/*
+ * fp32 router-weight multiply, forward.
+ * Defined on the page "nemo_automodel.components.moe.optimized_ops", entries
+ * _RouterWeightMulFunction (the forward equals the eager fp32 multiply bit
+ * for bit) and _rw_fwd_core:
+ *   out[r, k] = bf16( float32(x[r, k]) * probs[r] )      (one multiply, one rounding)
+ *   x     [rows, hidden] bf16 (expert down-projection output)   in
+ *   probs [rows] float32                                      in
+ *   out   [rows, hidden] bf16                                 out
+ * Returns a moe_epi_status.
+ */
+int router_weight_mul_fwd(const uint16_t *x, const float *probs, uint16_t *out,
+                          int64_t rows, int64_t hidden, void *stream);
+
+/*
+ * fp32 router-weight multiply, backward (both gradients in one pass over
+ * grad_out). Defined on the page "nemo_automodel.components.moe.optimized_ops",
+ * entries _RouterWeightMulFunction, _rw_bwd_x_core and _rw_bwd_probs_core:
+ *   grad_x[r, k]  = bf16( float32(grad_out[r, k]) * probs[r] )
+ *   grad_probs[r] = sum_k float32(grad_out[r, k]) * float32(x[r, k])   (float32, any order)
+ *   grad_out   [rows, hidden] bf16      in
+ *   x          [rows, hidden] bf16      in; may be NULL if and only if grad_probs is NULL
+ *   probs      [rows] float32           in
+ *   grad_x     [rows, hidden] bf16      out
+ *   grad_probs [rows] float32           out; may be NULL (the page's save_x = False case:
+ *                                       probabilities without gradient, x not kept)
+ * Returns a moe_epi_status.
+ */
+int router_weight_mul_bwd(const uint16_t *grad_out, const uint16_t *x, const float *probs,
+                          uint16_t *grad_x, float *grad_probs,
+                          int64_t rows, int64_t hidden, void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *moe_epi_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EPI_H */

@@ -1,1 +1,14 @@
-"""MI355X-native routed-expert epilogue (clamped SwiGLU x probs, fp32 router-weight multiply)."""
+"""MI355X-native routed-expert epilogue: clamped SwiGLU x routing probability and the
+fp32 router-weight multiply, each with a forward and a single-pass backward, as
+hand-written HIP kernels for gfx950 behind a C ABI (include/moe_epi.h).
+
+The binding loads libmoe_epi.so on first use and raises if it is not built.
+"""
+from .binding import (MoeEpiError, RouterWeightMul, SwigluClamped, router_weight_mul,
+                      router_weight_mul_bwd, router_weight_mul_fwd, swiglu_clamped,
+                      swiglu_clamped_bwd, swiglu_clamped_fwd)
+
+__all__ = [
+    "MoeEpiError", "RouterWeightMul", "SwigluClamped", "router_weight_mul", "router_weight_mul_bwd",
+    "router_weight_mul_fwd", "swiglu_clamped", "swiglu_clamped_bwd", "swiglu_clamped_fwd",
+]

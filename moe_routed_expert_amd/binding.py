@@ -1,0 +1,222 @@
+"""Python binding of libmoe_epi (ctypes; argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels. This module
+only checks that torch tensors have the dtypes, devices, shapes and
+contiguity the C ABI expects, passes their device pointers and the current
+HIP stream, and turns a nonzero status into an exception. PyTorch supplies
+device memory and streams. There is no fallback: if libmoe_epi.so is missing
+or fails to load, every call raises.
+
+Names follow the C ABI (include/moe_epi.h):
+  swiglu_clamped_fwd(x, probs, y, limit)
+  swiglu_clamped_bwd(x, probs, grad_y, grad_x, grad_probs, limit)
+  router_weight_mul_fwd(x, probs, out)
+  router_weight_mul_bwd(grad_out, x, probs, grad_x, grad_probs)
+plus allocating helpers and torch.autograd.Function wrappers with the shapes
+of the pages' SwigluClamped / _RouterWeightMulFunction.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_epi.so")
+
+STATUS = {
+    0: "MOE_EPI_SUCCESS",
+    1: "MOE_EPI_ERR_NULL_POINTER",
+    2: "MOE_EPI_ERR_BAD_SHAPE",
+    3: "MOE_EPI_ERR_BAD_LIMIT",
+    4: "MOE_EPI_ERR_ALIAS",
+    5: "MOE_EPI_ERR_MISALIGNED",
+    6: "MOE_EPI_ERR_LAUNCH",
+}
+
+_lib = None
+
+
+class MoeEpiError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({describe(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library. Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m moe_routed_expert_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    L.swiglu_clamped_fwd.argtypes = [vp, vp, vp, i64, i64, f32, vp]
+    L.swiglu_clamped_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, vp]
+    L.router_weight_mul_fwd.argtypes = [vp, vp, vp, i64, i64, vp]
+    L.router_weight_mul_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp]
+    for name in ("swiglu_clamped_fwd", "swiglu_clamped_bwd", "router_weight_mul_fwd", "router_weight_mul_bwd"):
+        getattr(L, name).restype = ctypes.c_int
+    L.moe_epi_status_string.argtypes = [ctypes.c_int]
+    L.moe_epi_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def describe(status: int) -> str:
+    return lib().moe_epi_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise MoeEpiError(status, where)
+
+
+def _stream_handle(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor | None, name: str, dtype, shape, device) -> None:
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError(f"{name}: expected a tensor on {device}, got {t.device}")
+    if tuple(t.shape) not in [tuple(s) for s in shape]:
+        raise ValueError(f"{name}: expected shape {' or '.join(str(tuple(s)) for s in shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+def _rows_cols(x: torch.Tensor, name: str):
+    if x.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got {tuple(x.shape)}")
+    return int(x.shape[0]), int(x.shape[1])
+
+
+# ---- C-ABI entry points -----------------------------------------------------
+
+def swiglu_clamped_fwd(x, probs, y, limit: float, stream=None) -> None:
+    """y[:] = bf16(silu(min(gate, L)) * clamp(up, -L, L) * probs); x = [gate | up] bf16
+    [rows, 2*inter]; probs fp32 [rows] or [rows, 1]; y bf16 [rows, inter]."""
+    rows, two_i = _rows_cols(x, "x")
+    if two_i % 2:
+        raise ValueError("x must have an even number of columns ([gate | up])")
+    inter, dev = two_i // 2, x.device
+    _need(x, "x", torch.bfloat16, [(rows, two_i)], dev)
+    _need(probs, "probs", torch.float32, [(rows,), (rows, 1)], dev)
+    _need(y, "y", torch.bfloat16, [(rows, inter)], dev)
+    _check(lib().swiglu_clamped_fwd(_ptr(x), _ptr(probs), _ptr(y), rows, inter, float(limit),
+                                    _stream_handle(x, stream)), "swiglu_clamped_fwd")
+
+
+def swiglu_clamped_bwd(x, probs, grad_y, grad_x, grad_probs, limit: float, stream=None) -> None:
+    """grad_x[:, :inter] = d_gate, grad_x[:, inter:] = d_up, grad_probs[:] = per-row
+    probability gradient (skipped when grad_probs is None)."""
+    rows, two_i = _rows_cols(x, "x")
+    if two_i % 2:
+        raise ValueError("x must have an even number of columns ([gate | up])")
+    inter, dev = two_i // 2, x.device
+    _need(x, "x", torch.bfloat16, [(rows, two_i)], dev)
+    _need(probs, "probs", torch.float32, [(rows,), (rows, 1)], dev)
+    _need(grad_y, "grad_y", torch.bfloat16, [(rows, inter)], dev)
+    _need(grad_x, "grad_x", torch.bfloat16, [(rows, two_i)], dev)
+    if grad_probs is not None:
+        _need(grad_probs, "grad_probs", torch.float32, [(rows,), (rows, 1)], dev)
+    _check(lib().swiglu_clamped_bwd(_ptr(x), _ptr(probs), _ptr(grad_y), _ptr(grad_x), _ptr(grad_probs),
+                                    rows, inter, float(limit), _stream_handle(x, stream)), "swiglu_clamped_bwd")
+
+
+def router_weight_mul_fwd(x, probs, out, stream=None) -> None:
+    """out[:] = bf16(fp32(x) * probs); x, out bf16 [rows, hidden]; probs fp32 [rows] or [rows, 1]."""
+    rows, hidden = _rows_cols(x, "x")
+    dev = x.device
+    _need(x, "x", torch.bfloat16, [(rows, hidden)], dev)
+    _need(probs, "probs", torch.float32, [(rows,), (rows, 1)], dev)
+    _need(out, "out", torch.bfloat16, [(rows, hidden)], dev)
+    _check(lib().router_weight_mul_fwd(_ptr(x), _ptr(probs), _ptr(out), rows, hidden,
+                                       _stream_handle(x, stream)), "router_weight_mul_fwd")
+
+
+def router_weight_mul_bwd(grad_out, x, probs, grad_x, grad_probs, stream=None) -> None:
+    """grad_x[:] = bf16(fp32(grad_out) * probs); grad_probs[:] = sum_k grad_out * x (fp32).
+    x and grad_probs may both be None (probabilities without gradient)."""
+    rows, hidden = _rows_cols(grad_out, "grad_out")
+    dev = grad_out.device
+    _need(grad_out, "grad_out", torch.bfloat16, [(rows, hidden)], dev)
+    if grad_probs is not None:
+        _need(x, "x", torch.bfloat16, [(rows, hidden)], dev)
+        _need(grad_probs, "grad_probs", torch.float32, [(rows,), (rows, 1)], dev)
+    _need(probs, "probs", torch.float32, [(rows,), (rows, 1)], dev)
+    _need(grad_x, "grad_x", torch.bfloat16, [(rows, hidden)], dev)
+    _check(lib().router_weight_mul_bwd(_ptr(grad_out), _ptr(x) if grad_probs is not None else None, _ptr(probs),
+                                       _ptr(grad_x), _ptr(grad_probs), rows, hidden,
+                                       _stream_handle(grad_out, stream)), "router_weight_mul_bwd")
+
+
+# ---- allocating helpers and autograd wrappers ------------------------------
+
+def swiglu_clamped(x, probs, limit: float):
+    y = torch.empty((x.shape[0], x.shape[1] // 2), dtype=torch.bfloat16, device=x.device)
+    swiglu_clamped_fwd(x, probs, y, limit)
+    return y
+
+
+def router_weight_mul(x, probs):
+    out = torch.empty_like(x)
+    router_weight_mul_fwd(x, probs, out)
+    return out
+
+
+class SwigluClamped(torch.autograd.Function):
+    """silu(clamp(gate, max=L)) * clamp(up, -L, L) * probs with the HIP forward and
+    single-pass backward; saves only x and probs."""
+
+    @staticmethod
+    def forward(ctx, x, probs, limit: float):
+        x = x.contiguous()
+        probs = probs.contiguous()
+        ctx.save_for_backward(x, probs)
+        ctx.limit = float(limit)
+        return swiglu_clamped(x, probs, limit)
+
+    @staticmethod
+    def backward(ctx, grad_y):
+        x, probs = ctx.saved_tensors
+        grad_x = torch.empty_like(x)
+        grad_probs = torch.empty_like(probs) if ctx.needs_input_grad[1] else None
+        swiglu_clamped_bwd(x, probs, grad_y.contiguous(), grad_x, grad_probs, ctx.limit)
+        return grad_x, grad_probs, None
+
+
+class RouterWeightMul(torch.autograd.Function):
+    """bf16(fp32(x) * probs) with the HIP forward and a one-pass backward. x is saved
+    only when probs needs a gradient (it is read only for that gradient)."""
+
+    @staticmethod
+    def forward(ctx, x, probs):
+        x = x.contiguous()
+        probs = probs.contiguous()
+        save_x = probs.requires_grad
+        ctx.save_for_backward(x if save_x else None, probs)
+        ctx.save_x = save_x
+        return router_weight_mul(x, probs)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        x, probs = ctx.saved_tensors
+        grad_out = grad_out.contiguous()
+        grad_x = torch.empty_like(grad_out)
+        grad_probs = torch.empty_like(probs) if ctx.save_x else None
+        router_weight_mul_bwd(grad_out, x, probs, grad_x, grad_probs)
+        return grad_x, grad_probs

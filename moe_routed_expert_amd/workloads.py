@@ -30,11 +30,14 @@ Readings taken where the workload text is loose:
     group's sum, computed in float64 and rounded once to float32;
   - normals are drawn in float32, scaled by sigma in float32 and rounded to
     bfloat16 to nearest-even.
-Draws are made in fixed chunks of rows from independent streams spawned from
-numpy.random.SeedSequence(seed), so a workload is the same on every machine.
+Draws are made in fixed chunks of 4096 rows; each chunk and each kind of draw
+has its own PCG64 stream from numpy.random.SeedSequence(seed, spawn_key=(kind,
+chunk)), so a workload is the same on every machine and for any thread count.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -83,39 +86,53 @@ class Workload:
             return self.rows * (6 * self.cols + 8)
         return self.rows * (4 * self.cols + 4)
 
-    def generate(self, rows: int | None = None) -> dict:
+    def generate(self, rows: int | None = None, threads: int | None = None) -> dict:
         """Inputs as numpy arrays: x (uint16 bf16 bits [rows, x_cols]),
         probs (float32 [rows]), grad_out (uint16 bf16 bits [rows, cols]).
 
-        rows < self.rows gives the leading rows of the same workload (the same
-        values as the full draw, for the chunks it covers)."""
+        Each chunk of CHUNK_ROWS rows draws from its own streams, derived from
+        (seed, stream kind, chunk index), so chunks can be drawn in parallel and
+        rows < self.rows gives exactly the leading rows of the full workload."""
         n = self.rows if rows is None else int(rows)
         if n < 0 or n > self.rows:
             raise ValueError("rows out of range")
-        ss = np.random.SeedSequence(self.seed)
-        s_x, s_xmask, s_p, s_pmask, s_gy = [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(5)]
         xc, gc = self.x_cols, self.cols
         x = np.empty((n, xc), dtype=np.uint16)
         gy = np.empty((n, gc), dtype=np.uint16)
         special = np.array(self.x_special_values, dtype=np.float32)
-        for r0 in range(0, n, CHUNK_ROWS):
+
+        def rng(kind: int, chunk: int) -> np.random.Generator:
+            return np.random.Generator(np.random.PCG64(np.random.SeedSequence(self.seed, spawn_key=(kind, chunk))))
+
+        def fill(chunk: int) -> None:
+            r0 = chunk * CHUNK_ROWS
             m = min(CHUNK_ROWS, n - r0)
-            xf = s_x.standard_normal((m, xc), dtype=np.float32)
+            xf = rng(0, chunk).standard_normal((m, xc), dtype=np.float32)
             xf *= np.float32(self.x_sigma)
             if self.x_special_frac > 0.0:
-                hit = s_xmask.random((m, xc), dtype=np.float32) < np.float32(self.x_special_frac)
-                pick = s_xmask.integers(0, len(special), size=int(hit.sum()))
-                xf[hit] = special[pick]
+                g = rng(1, chunk)
+                hit = g.random((m, xc), dtype=np.float32) < np.float32(self.x_special_frac)
+                xf[hit] = special[g.integers(0, len(special), size=int(hit.sum()))]
             x[r0:r0 + m] = _to_bf16_bits(xf)
-            gy[r0:r0 + m] = _to_bf16_bits(s_gy.standard_normal((m, gc), dtype=np.float32))
-        probs = s_p.random(self.rows, dtype=np.float32)[:n].copy()
+            gy[r0:r0 + m] = _to_bf16_bits(rng(2, chunk).standard_normal((m, gc), dtype=np.float32))
+
+        chunks = range((n + CHUNK_ROWS - 1) // CHUNK_ROWS)
+        workers = threads or max(1, min(16, os.cpu_count() or 1))
+        if workers > 1 and len(chunks) > 1:
+            with ThreadPoolExecutor(workers) as pool:
+                list(pool.map(fill, chunks))
+        else:
+            for c in chunks:
+                fill(c)
+
+        probs = rng(3, 0).random(self.rows, dtype=np.float32)[:n].copy()
         if self.probs_kind == "top8":
             p64 = probs.astype(np.float64)
             for g0 in range(0, n, 8):
                 p64[g0:g0 + 8] /= p64[g0:g0 + 8].sum()
             probs = p64.astype(np.float32)
         elif self.probs_kind == "uniform_zeros":
-            zero = s_pmask.random(self.rows, dtype=np.float32)[:n] < np.float32(self.probs_zero_frac)
+            zero = rng(4, 0).random(self.rows, dtype=np.float32)[:n] < np.float32(self.probs_zero_frac)
             probs[zero] = np.float32(0.0)
         elif self.probs_kind != "uniform":
             raise ValueError(self.probs_kind)

@@ -23,6 +23,7 @@ _lib = None
 
 _u16p = ctypes.POINTER(ctypes.c_uint16)
 _f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
 _i64 = ctypes.c_int64
 
 
@@ -47,12 +48,13 @@ def _load():
     lib.oracle_swiglu_point.restype = None
     lib.oracle_swiglu_clamped_fwd.argtypes = [_u16p, _f32p, _u16p, _i64, _i64, ctypes.c_float, ctypes.c_int]
     lib.oracle_swiglu_clamped_fwd.restype = None
-    lib.oracle_swiglu_clamped_bwd.argtypes = [_u16p, _f32p, _u16p, _u16p, _f32p, _i64, _i64,
+    lib.oracle_swiglu_clamped_bwd.argtypes = [_u16p, _f32p, _u16p, _u16p, _f32p, _f64p, _i64, _i64,
                                               ctypes.c_float, ctypes.c_int]
     lib.oracle_swiglu_clamped_bwd.restype = None
     lib.oracle_router_weight_mul_fwd.argtypes = [_u16p, _f32p, _u16p, _i64, _i64, ctypes.c_int]
     lib.oracle_router_weight_mul_fwd.restype = None
-    lib.oracle_router_weight_mul_bwd.argtypes = [_u16p, _u16p, _f32p, _u16p, _f32p, _i64, _i64, ctypes.c_int]
+    lib.oracle_router_weight_mul_bwd.argtypes = [_u16p, _u16p, _f32p, _u16p, _f32p, _f64p, _i64, _i64,
+                                                 ctypes.c_int]
     lib.oracle_router_weight_mul_bwd.restype = None
     _lib = lib
     return lib
@@ -108,17 +110,22 @@ def swiglu_clamped_fwd(x, probs, rows, inter, L, threads=None):
     return y
 
 
-def swiglu_clamped_bwd(x, probs, grad_y, rows, inter, L, want_grad_probs=True, threads=None):
-    """(grad_x uint16 [rows, 2*inter], grad_probs float32 [rows] or None)."""
+def swiglu_clamped_bwd(x, probs, grad_y, rows, inter, L, want_grad_probs=True, threads=None,
+                       with_abs_sum=False):
+    """(grad_x uint16 [rows, 2*inter], grad_probs float32 [rows] or None), plus the
+    per-row sum of |term| (float64) when with_abs_sum."""
     x = _arr(x, np.uint16, (rows, 2 * inter))
     probs = _arr(probs, np.float32, (rows,))
     grad_y = _arr(grad_y, np.uint16, (rows, inter))
     grad_x = np.empty((rows, 2 * inter), dtype=np.uint16)
     grad_probs = np.empty((rows,), dtype=np.float32) if want_grad_probs else None
+    abs_sum = np.empty((rows,), dtype=np.float64) if with_abs_sum else None
     _load().oracle_swiglu_clamped_bwd(_p(x, ctypes.c_uint16), _p(probs, ctypes.c_float),
                                       _p(grad_y, ctypes.c_uint16), _p(grad_x, ctypes.c_uint16),
-                                      _p(grad_probs, ctypes.c_float), rows, inter, float(L),
-                                      threads or default_threads())
+                                      _p(grad_probs, ctypes.c_float), _p(abs_sum, ctypes.c_double),
+                                      rows, inter, float(L), threads or default_threads())
+    if with_abs_sum:
+        return grad_x, grad_probs, abs_sum
     return grad_x, grad_probs
 
 
@@ -133,9 +140,11 @@ def router_weight_mul_fwd(x, probs, rows, hidden, threads=None):
     return out
 
 
-def router_weight_mul_bwd(grad_out, x, probs, rows, hidden, want_grad_probs=True, threads=None):
-    """(grad_x uint16 [rows, hidden], grad_probs float32 [rows] or None); x may be None
-    when want_grad_probs is False."""
+def router_weight_mul_bwd(grad_out, x, probs, rows, hidden, want_grad_probs=True, threads=None,
+                          with_abs_sum=False):
+    """(grad_x uint16 [rows, hidden], grad_probs float32 [rows] or None), plus the
+    per-row sum of |term| (float64) when with_abs_sum; x may be None when
+    want_grad_probs is False."""
     grad_out = _arr(grad_out, np.uint16, (rows, hidden))
     if want_grad_probs:
         x = _arr(x, np.uint16, (rows, hidden))
@@ -144,8 +153,11 @@ def router_weight_mul_bwd(grad_out, x, probs, rows, hidden, want_grad_probs=True
     probs = _arr(probs, np.float32, (rows,))
     grad_x = np.empty((rows, hidden), dtype=np.uint16)
     grad_probs = np.empty((rows,), dtype=np.float32) if want_grad_probs else None
+    abs_sum = np.empty((rows,), dtype=np.float64) if (with_abs_sum and want_grad_probs) else None
     _load().oracle_router_weight_mul_bwd(_p(grad_out, ctypes.c_uint16), _p(x, ctypes.c_uint16),
                                          _p(probs, ctypes.c_float), _p(grad_x, ctypes.c_uint16),
-                                         _p(grad_probs, ctypes.c_float), rows, hidden,
-                                         threads or default_threads())
+                                         _p(grad_probs, ctypes.c_float), _p(abs_sum, ctypes.c_double),
+                                         rows, hidden, threads or default_threads())
+    if with_abs_sum:
+        return grad_x, grad_probs, abs_sum
     return grad_x, grad_probs

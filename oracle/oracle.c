@@ -129,9 +129,12 @@ void oracle_swiglu_clamped_fwd(const uint16_t *x, const float *probs, uint16_t *
 
 /* [SW] backward. grad_y is [rows, inter]; grad_x is [rows, 2*inter] with
  * d_gate in the first half of each row and d_up in the second; grad_probs is
- * [rows] and may be NULL, in which case no probability gradient is formed. */
+ * [rows] and may be NULL, in which case no probability gradient is formed.
+ * grad_probs_abs (may be NULL) receives sum_j |term_j| per row in binary64:
+ * the scale against which a probability gradient summed in another order is
+ * judged. */
 void oracle_swiglu_clamped_bwd(const uint16_t *x, const float *probs, const uint16_t *grad_y,
-                               uint16_t *grad_x, float *grad_probs,
+                               uint16_t *grad_x, float *grad_probs, double *grad_probs_abs,
                                int64_t rows, int64_t inter, float L, int nthreads)
 {
     int64_t r;
@@ -140,7 +143,7 @@ void oracle_swiglu_clamped_bwd(const uint16_t *x, const float *probs, const uint
         const uint16_t *xr = x + r * 2 * inter;
         const uint16_t *gyr = grad_y + r * inter;
         uint16_t *gxr = grad_x + r * 2 * inter;
-        double acc = 0.0;
+        double acc = 0.0, acc_abs = 0.0;
         for (int64_t j = 0; j < inter; ++j) {
             float q[4];
             oracle_swiglu_point(oracle_bf16_to_f32(xr[j]), oracle_bf16_to_f32(xr[inter + j]),
@@ -148,9 +151,12 @@ void oracle_swiglu_clamped_bwd(const uint16_t *x, const float *probs, const uint
             gxr[j] = oracle_f32_to_bf16(q[1]);
             gxr[inter + j] = oracle_f32_to_bf16(q[2]);
             acc += (double)q[3];
+            acc_abs += fabs((double)q[3]);
         }
         if (grad_probs)
             grad_probs[r] = (float)acc;
+        if (grad_probs_abs)
+            grad_probs_abs[r] = acc_abs;
     }
 }
 
@@ -175,22 +181,28 @@ void oracle_router_weight_mul_fwd(const uint16_t *x, const float *probs, uint16_
  *   grad_x[r,k]   = bf16(fp32(grad_out[r,k]) * p[r])
  *   grad_probs[r] = sum_k fp32(grad_out[r,k]) * fp32(x[r,k])
  * grad_probs may be NULL (probabilities that carry no gradient); x is then
- * not read and may be NULL too. */
+ * not read and may be NULL too. grad_probs_abs (may be NULL) receives
+ * sum_k |term_k| per row in binary64, the scale of the sum. */
 void oracle_router_weight_mul_bwd(const uint16_t *grad_out, const uint16_t *x, const float *probs,
-                                  uint16_t *grad_x, float *grad_probs,
+                                  uint16_t *grad_x, float *grad_probs, double *grad_probs_abs,
                                   int64_t rows, int64_t hidden, int nthreads)
 {
     int64_t r;
 #pragma omp parallel for schedule(static) num_threads(nthreads)
     for (r = 0; r < rows; ++r) {
-        double acc = 0.0;
+        double acc = 0.0, acc_abs = 0.0;
         for (int64_t k = 0; k < hidden; ++k) {
             float g = oracle_bf16_to_f32(grad_out[r * hidden + k]);
             grad_x[r * hidden + k] = oracle_f32_to_bf16(g * probs[r]);
-            if (grad_probs)
-                acc += (double)(g * oracle_bf16_to_f32(x[r * hidden + k]));
+            if (grad_probs) {
+                float term = g * oracle_bf16_to_f32(x[r * hidden + k]);
+                acc += (double)term;
+                acc_abs += fabs((double)term);
+            }
         }
         if (grad_probs)
             grad_probs[r] = (float)acc;
+        if (grad_probs && grad_probs_abs)
+            grad_probs_abs[r] = acc_abs;
     }
 }

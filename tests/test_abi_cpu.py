@@ -1,0 +1,140 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/moe_epi.h declares, and rejects bad arguments on the host before any
+HIP call. Every call here is built to fail validation (or to have rows == 0),
+so nothing is ever launched."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+import torch
+
+from moe_routed_expert_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# Host-only checks: where a GPU is visible they are not needed (and a mistaken
+# case that passed validation would launch on fake addresses), so skip there.
+pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0, reason="host-only checks; a GPU is visible")
+
+OK, NULLP, SHAPE, LIMIT, ALIAS, MISAL, LAUNCH = range(7)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        from moe_routed_expert_amd import build
+        build.build()
+    return binding.lib()
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\([^;]*\)\s*;", text, flags=re.M)
+    return names
+
+
+def test_header_declares_the_four_ops_and_status_string():
+    assert set(declared_functions()) >= {"swiglu_clamped_fwd", "swiglu_clamped_bwd", "router_weight_mul_fwd",
+                                         "router_weight_mul_bwd", "moe_epi_status_string"}
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code in range(7):
+        s = binding.describe(code)
+        assert s and s != "unknown status"
+    assert binding.describe(99) == "unknown status"
+    assert binding.describe(0) == "success"
+
+
+# fake, never dereferenced device addresses (validation fails before any use)
+A = 0x10_0000_0000
+B = 0x20_0000_0000
+C = 0x30_0000_0000
+D = 0x40_0000_0000
+E = 0x50_0000_0000
+
+
+def sw_fwd(L, x, p, y, rows=4, inter=8, lim=7.0):
+    return L.swiglu_clamped_fwd(x, p, y, rows, inter, lim, None)
+
+
+def sw_bwd(L, x, p, gy, gx, gp, rows=4, inter=8, lim=7.0):
+    return L.swiglu_clamped_bwd(x, p, gy, gx, gp, rows, inter, lim, None)
+
+
+def test_swiglu_fwd_validation(L):
+    assert sw_fwd(L, None, B, C) == NULLP
+    assert sw_fwd(L, A, None, C) == NULLP
+    assert sw_fwd(L, A, B, None) == NULLP
+    assert sw_fwd(L, A, B, C, rows=-1) == SHAPE
+    assert sw_fwd(L, A, B, C, inter=0) == SHAPE
+    assert sw_fwd(L, A, B, C, inter=-3) == SHAPE
+    assert sw_fwd(L, A, B, C, rows=1 << 40, inter=1 << 40) == SHAPE
+    for bad in (0.0, -1.0, float("inf"), float("nan"), -0.0):
+        assert sw_fwd(L, A, B, C, lim=bad) == LIMIT
+    assert sw_fwd(L, A + 1, B, C) == MISAL
+    assert sw_fwd(L, A, B + 2, C) == MISAL
+    assert sw_fwd(L, A, B, C + 1) == MISAL
+    # x is 4 x 16 bf16 = 128 bytes: y inside it, or probs inside y, is aliasing
+    assert sw_fwd(L, A, B, A + 64) == ALIAS
+    assert sw_fwd(L, A, B, A + 126) == ALIAS
+    assert sw_fwd(L, A, C + 16, C) == ALIAS
+    # rows == 0 launches nothing and accepts NULL buffers
+    assert sw_fwd(L, None, None, None, rows=0) == OK
+    assert sw_fwd(L, None, None, None, rows=0, lim=0.0) == LIMIT
+
+
+def test_swiglu_bwd_validation(L):
+    assert sw_bwd(L, None, B, C, D, E) == NULLP
+    assert sw_bwd(L, A, B, None, D, E) == NULLP
+    assert sw_bwd(L, A, B, C, None, E) == NULLP
+    assert sw_bwd(L, A, B, C, D, E, inter=0) == SHAPE
+    assert sw_bwd(L, A, B, C, D, E, lim=float("nan")) == LIMIT
+    assert sw_bwd(L, A, B, C, D + 1, E) == MISAL
+    assert sw_bwd(L, A, B, C, D, E + 2) == MISAL
+    assert sw_bwd(L, A, B, C, A + 2, E) == ALIAS       # grad_x over x
+    assert sw_bwd(L, A, B, C, C, E) == ALIAS           # grad_x over grad_y
+    assert sw_bwd(L, A, B, C, D, D + 64) == ALIAS      # grad_probs inside grad_x
+    assert sw_bwd(L, A, B, C, D, B) == ALIAS           # grad_probs over probs
+    assert sw_bwd(L, None, None, None, None, None, rows=0) == OK
+
+
+def test_router_validation(L):
+    f = lambda x, p, o, rows=4, h=8: L.router_weight_mul_fwd(x, p, o, rows, h, None)
+    b = lambda go, x, p, gx, gp, rows=4, h=8: L.router_weight_mul_bwd(go, x, p, gx, gp, rows, h, None)
+    assert f(None, B, C) == NULLP
+    assert f(A, B, C, rows=-2) == SHAPE
+    assert f(A, B, C, h=0) == SHAPE
+    assert f(A + 1, B, C) == MISAL
+    assert f(A, B, A + 8) == ALIAS
+    assert f(None, None, None, rows=0) == OK
+    assert b(A, None, C, D, E) == NULLP                # grad_probs wanted but no x
+    assert b(None, B, C, D, None) == NULLP
+    assert b(A, B, C, D, E, h=-1) == SHAPE
+    assert b(A, B, C, D + 1, E) == MISAL
+    assert b(A, B, C, A + 16, E) == ALIAS              # grad_x over grad_out
+    assert b(A, B, C, D, D) == ALIAS                   # grad_probs over grad_x
+    assert b(A, B, C, D + 3, None) == MISAL            # odd grad_x address
+    assert b(None, None, None, None, None, rows=0) == OK
+
+
+def test_binding_rejects_cpu_tensors_before_the_library():
+    x = torch.zeros(4, 16, dtype=torch.bfloat16)
+    p = torch.zeros(4, dtype=torch.float32)
+    y = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.swiglu_clamped_fwd(x, p, y, 7.0)
+    with pytest.raises(TypeError):
+        binding.swiglu_clamped_fwd(x.float(), p, y, 7.0)
+    with pytest.raises(ValueError):
+        binding.router_weight_mul_fwd(x[:, :7], p, y[:, :7])
