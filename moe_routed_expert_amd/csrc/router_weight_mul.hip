@@ -11,84 +11,88 @@
 // grad_out; here both come out of one pass (grad_out and x read once).
 //
 // Kernel shape: as for the SwiGLU kernels, a lane group of G lanes owns a row
-// and walks it in 16-byte vectors (8 bf16), V vectors per lane in flight; the
-// row sum is a register accumulator reduced with cross-lane shuffles. The
-// forward needs no reduction but uses the same row walk, which loads the
-// row's probability once and needs no division to find a vector's row.
+// and walks it in 16-byte nontemporal vectors (8 bf16), V vectors per lane in
+// flight (hidden = 7168: 896 vectors, 7 per lane, 2 passes); the row sum is a
+// register accumulator reduced with cross-lane shuffles. The forward needs no
+// reduction but uses the same row walk, which loads the row's probability
+// once and needs no division to find a vector's row.
 #include "epi_common.h"
 
 namespace moe_epi {
 namespace {
 
-template <int W, int G, int V>
+constexpr int kBlock = 256;
+constexpr int kVmax = 8;
+
+template <int G, int V>
 __global__ __launch_bounds__(kBlock) void router_weight_mul_fwd_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ probs, uint16_t* __restrict__ out, int64_t rows,
     int64_t hidden) {
-    constexpr int kGroups = kBlock / G;
-    const int lane = threadIdx.x & (G - 1);
-    const int64_t nvec = hidden / W;
-    const int64_t row_step = static_cast<int64_t>(gridDim.x) * kGroups;
-    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kGroups + threadIdx.x / G; r < rows; r += row_step) {
+    constexpr int kRows = kBlock / G;
+    const int lane = threadIdx.x % G;
+    const int64_t nvec = hidden / 8;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kRows + threadIdx.x / G; r < rows;
+         r += static_cast<int64_t>(gridDim.x) * kRows) {
         const uint16_t* xr = x + r * hidden;
         uint16_t* orow = out + r * hidden;
         const float p = probs[r];
         for (int64_t c0 = lane; c0 < nvec; c0 += static_cast<int64_t>(G) * V) {
-            float v[V][W];
+            u32x4 v[V];
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                if (c0 + k * G < nvec) v[k] = load_stream(xr + (c0 + k * G) * 8);
 #pragma unroll
             for (int k = 0; k < V; ++k) {
-                const int64_t c = c0 + static_cast<int64_t>(k) * G;
-                if (c < nvec) Io<W>::load(xr + c * W, v[k]);
-            }
+                if (c0 + k * G < nvec) {
+                    u32x4 o;
 #pragma unroll
-            for (int k = 0; k < V; ++k) {
-                const int64_t c = c0 + static_cast<int64_t>(k) * G;
-                if (c < nvec) {
-                    float o[W];
-#pragma unroll
-                    for (int e = 0; e < W; ++e) o[e] = v[k][e] * p;
-                    Io<W>::store(orow + c * W, o);
+                    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(bf16_lo(v[k][i]) * p, bf16_hi(v[k][i]) * p);
+                    store_stream(orow + (c0 + k * G) * 8, o);
                 }
             }
         }
     }
 }
 
-template <int W, int G, int V, bool kGradProbs>
+template <int G, int V, bool kGradProbs>
 __global__ __launch_bounds__(kBlock) void router_weight_mul_bwd_kernel(
     const uint16_t* __restrict__ grad_out, const uint16_t* __restrict__ x, const float* __restrict__ probs,
     uint16_t* __restrict__ grad_x, float* __restrict__ grad_probs, int64_t rows, int64_t hidden) {
-    constexpr int kGroups = kBlock / G;
-    const int lane = threadIdx.x & (G - 1);
-    const int64_t nvec = hidden / W;
-    const int64_t row_step = static_cast<int64_t>(gridDim.x) * kGroups;
-    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kGroups + threadIdx.x / G; r < rows; r += row_step) {
+    constexpr int kRows = kBlock / G;
+    const int lane = threadIdx.x % G;
+    const int64_t nvec = hidden / 8;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kRows + threadIdx.x / G; r < rows;
+         r += static_cast<int64_t>(gridDim.x) * kRows) {
         const uint16_t* gr = grad_out + r * hidden;
         const uint16_t* xr = x + r * hidden;
         uint16_t* gxr = grad_x + r * hidden;
         const float p = probs[r];
         float acc = 0.0f;
         for (int64_t c0 = lane; c0 < nvec; c0 += static_cast<int64_t>(G) * V) {
-            float g[V][W], xv[V][W];
+            u32x4 g[V], xv[V];
 #pragma unroll
-            for (int k = 0; k < V; ++k) {
-                const int64_t c = c0 + static_cast<int64_t>(k) * G;
-                if (c < nvec) {
-                    Io<W>::load(gr + c * W, g[k]);
-                    if (kGradProbs) Io<W>::load(xr + c * W, xv[k]);
-                }
+            for (int k = 0; k < V; ++k)
+                if (c0 + k * G < nvec) g[k] = load_stream(gr + (c0 + k * G) * 8);
+            if (kGradProbs) {
+#pragma unroll
+                for (int k = 0; k < V; ++k)
+                    if (c0 + k * G < nvec) xv[k] = load_stream(xr + (c0 + k * G) * 8);
             }
 #pragma unroll
             for (int k = 0; k < V; ++k) {
-                const int64_t c = c0 + static_cast<int64_t>(k) * G;
-                if (c < nvec) {
-                    float o[W];
+                if (c0 + k * G < nvec) {
+                    u32x4 o;
 #pragma unroll
-                    for (int e = 0; e < W; ++e) {
-                        o[e] = g[k][e] * p;
+                    for (int i = 0; i < 4; ++i) {
+                        const float g0 = bf16_lo(g[k][i]), g1 = bf16_hi(g[k][i]);
+                        o[i] = pack_bf16x2(g0 * p, g1 * p);
                         // a product of two bf16 values is exact in fp32
-                        if (kGradProbs) acc = __fmaf_rn(g[k][e], xv[k][e], acc);
+                        if (kGradProbs) {
+                            acc = __fmaf_rn(g0, bf16_lo(xv[k][i]), acc);
+                            acc = __fmaf_rn(g1, bf16_hi(xv[k][i]), acc);
+                        }
                     }
-                    Io<W>::store(gxr + c * W, o);
+                    store_stream(gxr + (c0 + k * G) * 8, o);
                 }
             }
         }
@@ -99,51 +103,58 @@ __global__ __launch_bounds__(kBlock) void router_weight_mul_bwd_kernel(
     }
 }
 
-struct Shape {
-    int G, V;
-};
-
-inline Shape pick_shape(int64_t nvec) {
-    if (nvec >= 64) {
-        int64_t v = (nvec + 63) / 64;
-        return Shape{64, static_cast<int>(v > 4 ? 4 : v)};
+// per-element kernels (any hidden, 2-byte aligned tensors)
+__global__ __launch_bounds__(kBlock) void router_weight_mul_fwd_scalar_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ probs, uint16_t* __restrict__ out, int64_t rows,
+    int64_t hidden) {
+    constexpr int kRows = kBlock / 64;
+    const int lane = threadIdx.x % 64;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kRows + threadIdx.x / 64; r < rows;
+         r += static_cast<int64_t>(gridDim.x) * kRows) {
+        const float p = probs[r];
+        for (int64_t k = lane; k < hidden; k += 64) out[r * hidden + k] = to_bf16(bf16_at(x + r * hidden + k) * p);
     }
-    if (nvec > 16) return Shape{32, 1};
-    if (nvec > 8) return Shape{16, 1};
-    return Shape{8, 1};
 }
 
-constexpr int64_t kMaxBlocks = 1 << 20;  // 2^28 work-items at most; the row loop strides over the rest
+template <bool kGradProbs>
+__global__ __launch_bounds__(kBlock) void router_weight_mul_bwd_scalar_kernel(
+    const uint16_t* __restrict__ grad_out, const uint16_t* __restrict__ x, const float* __restrict__ probs,
+    uint16_t* __restrict__ grad_x, float* __restrict__ grad_probs, int64_t rows, int64_t hidden) {
+    constexpr int kRows = kBlock / 64;
+    const int lane = threadIdx.x % 64;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kRows + threadIdx.x / 64; r < rows;
+         r += static_cast<int64_t>(gridDim.x) * kRows) {
+        const float p = probs[r];
+        float acc = 0.0f;
+        for (int64_t k = lane; k < hidden; k += 64) {
+            const float g = bf16_at(grad_out + r * hidden + k);
+            grad_x[r * hidden + k] = to_bf16(g * p);
+            if (kGradProbs) acc = __fmaf_rn(g, bf16_at(x + r * hidden + k), acc);
+        }
+        if (kGradProbs) {
+            acc = group_sum<64>(acc);
+            if (lane == 0) grad_probs[r] = acc;
+        }
+    }
+}
 
-template <int W, int G, int V>
+template <int G, int V>
 void launch_fwd(const uint16_t* x, const float* probs, uint16_t* out, int64_t rows, int64_t hidden, hipStream_t st) {
-    const unsigned grid = grid_for_rows(rows, kBlock / G, kMaxBlocks);
-    hipLaunchKernelGGL((router_weight_mul_fwd_kernel<W, G, V>), dim3(grid), dim3(kBlock), 0, st, x, probs, out, rows,
-                       hidden);
+    hipLaunchKernelGGL((router_weight_mul_fwd_kernel<G, V>), dim3(grid_for_rows(rows, kBlock / G)), dim3(kBlock), 0,
+                       st, x, probs, out, rows, hidden);
 }
 
-template <int W, int G, int V>
+template <int G, int V>
 void launch_bwd(const uint16_t* go, const uint16_t* x, const float* probs, uint16_t* gx, float* gp, int64_t rows,
                 int64_t hidden, hipStream_t st) {
-    const unsigned grid = grid_for_rows(rows, kBlock / G, kMaxBlocks);
+    const dim3 grid(grid_for_rows(rows, kBlock / G));
     if (gp)
-        hipLaunchKernelGGL((router_weight_mul_bwd_kernel<W, G, V, true>), dim3(grid), dim3(kBlock), 0, st, go, x,
-                           probs, gx, gp, rows, hidden);
+        hipLaunchKernelGGL((router_weight_mul_bwd_kernel<G, V, true>), grid, dim3(kBlock), 0, st, go, x, probs, gx,
+                           gp, rows, hidden);
     else
-        hipLaunchKernelGGL((router_weight_mul_bwd_kernel<W, G, V, false>), dim3(grid), dim3(kBlock), 0, st, go, x,
-                           probs, gx, gp, rows, hidden);
+        hipLaunchKernelGGL((router_weight_mul_bwd_kernel<G, V, false>), grid, dim3(kBlock), 0, st, go, x, probs, gx,
+                           gp, rows, hidden);
 }
-
-#define MOE_EPI_DISPATCH_SHAPE(SHAPE, LAUNCH, ...)                          \
-    do {                                                                    \
-        if ((SHAPE).G == 64 && (SHAPE).V == 4) LAUNCH<8, 64, 4>(__VA_ARGS__); \
-        else if ((SHAPE).G == 64 && (SHAPE).V == 3) LAUNCH<8, 64, 3>(__VA_ARGS__); \
-        else if ((SHAPE).G == 64 && (SHAPE).V == 2) LAUNCH<8, 64, 2>(__VA_ARGS__); \
-        else if ((SHAPE).G == 64) LAUNCH<8, 64, 1>(__VA_ARGS__);            \
-        else if ((SHAPE).G == 32) LAUNCH<8, 32, 1>(__VA_ARGS__);            \
-        else if ((SHAPE).G == 16) LAUNCH<8, 16, 1>(__VA_ARGS__);            \
-        else LAUNCH<8, 8, 1>(__VA_ARGS__);                                  \
-    } while (0)
 
 int check_router(int64_t rows, int64_t hidden, int64_t* h_bytes, int64_t* p_bytes) {
     if (rows < 0 || hidden <= 0) return MOE_EPI_ERR_BAD_SHAPE;
@@ -169,10 +180,11 @@ extern "C" int router_weight_mul_fwd(const uint16_t* x, const float* probs, uint
     hipStream_t s = as_stream(stream);
     (void)hipGetLastError();
     if (hidden % 8 == 0 && aligned(x, 16) && aligned(out, 16)) {
-        const Shape sh = pick_shape(hidden / 8);
+        const Shape sh = pick_shape(hidden / 8, kVmax);
         MOE_EPI_DISPATCH_SHAPE(sh, launch_fwd, x, probs, out, rows, hidden, s);
     } else {
-        launch_fwd<1, 64, 4>(x, probs, out, rows, hidden, s);
+        hipLaunchKernelGGL(router_weight_mul_fwd_scalar_kernel, dim3(grid_for_rows(rows, kBlock / 64)), dim3(kBlock),
+                           0, s, x, probs, out, rows, hidden);
     }
     return launch_status();
 }
@@ -199,10 +211,16 @@ extern "C" int router_weight_mul_bwd(const uint16_t* grad_out, const uint16_t* x
     hipStream_t s = as_stream(stream);
     (void)hipGetLastError();
     if (hidden % 8 == 0 && aligned(grad_out, 16) && aligned(grad_x, 16) && (!x || aligned(x, 16))) {
-        const Shape sh = pick_shape(hidden / 8);
+        const Shape sh = pick_shape(hidden / 8, kVmax);
         MOE_EPI_DISPATCH_SHAPE(sh, launch_bwd, grad_out, x, probs, grad_x, grad_probs, rows, hidden, s);
     } else {
-        launch_bwd<1, 64, 4>(grad_out, x, probs, grad_x, grad_probs, rows, hidden, s);
+        const dim3 grid(grid_for_rows(rows, kBlock / 64));
+        if (grad_probs)
+            hipLaunchKernelGGL(router_weight_mul_bwd_scalar_kernel<true>, grid, dim3(kBlock), 0, s, grad_out, x,
+                               probs, grad_x, grad_probs, rows, hidden);
+        else
+            hipLaunchKernelGGL(router_weight_mul_bwd_scalar_kernel<false>, grid, dim3(kBlock), 0, s, grad_out, x,
+                               probs, grad_x, grad_probs, rows, hidden);
     }
     return launch_status();
 }

@@ -11,23 +11,32 @@
 // masks on the input values.
 //
 // Kernel shape (MI355X-first, not the page's Triton tiling):
-//   * A lane group of G lanes owns one row at a time (G = 64: a whole
-//     wavefront per row). Lane l of the group handles vectors l, l + G, ...
-//     of the row, each vector being 8 consecutive bf16 columns (16 bytes), so
-//     every wavefront-wide access is 1 KiB contiguous for each of gate, up,
-//     grad_y and the outputs. V vectors per lane are loaded before any math
-//     to keep 2V (forward) or 3V (backward) 16-byte loads in flight per lane.
+//   * A lane group of G lanes owns one row (G = 64: a wavefront per row).
+//     Lane l handles 16-byte vectors l, l + G, ... of the row, so each
+//     wavefront-wide access is 1 KiB contiguous in gate, up, grad_y and the
+//     outputs. All V vectors of a pass are loaded (gate, then up, then grad_y)
+//     before any math, so 2V (forward) or 3V (backward) 16-byte loads per lane
+//     are in flight; with V = 4 at inter = 2048 one pass covers the row.
+//   * Blocks of 256 threads (forward) and 128 threads (backward), one row per
+//     wavefront: the shapes that sustained the most bandwidth on MI355X among
+//     64-512 thread blocks, persistent grids and register double-buffering
+//     across rows.
 //   * The probability gradient is a per-lane fp32 register accumulator,
 //     reduced across the G lanes with cross-lane shuffles; no LDS.
-//   * This is elementwise streaming work: no MFMA, no LDS tiles. Each input
-//     byte is read once and each output byte written once.
-//   * Math per element: 2 compares/selects for the clamps, exp via v_exp_f32
-//     and 1/(1+e) via v_rcp_f32, the rest fp32 multiplies in the same order
-//     as the defining expression (built with -ffp-contract=off).
+//   * Elementwise streaming work: no MFMA, no LDS tiles, each input byte read
+//     once and each output byte written once (nontemporal accesses).
+//   * Math per element: compare/select clamps (NaN passes through, as in
+//     torch.clamp), exp via v_exp_f32 and 1/(1+e) via v_rcp_f32, the rest
+//     fp32 multiplies in the order of the defining expression (built with
+//     -ffp-contract=off).
 #include "epi_common.h"
 
 namespace moe_epi {
 namespace {
+
+constexpr int kFwdBlock = 256;
+constexpr int kBwdBlock = 128;
+constexpr int kVmax = 4;
 
 // sigma(z) = 1 / (1 + e^-z) with e^-z = 2^(-z * log2(e)).
 __device__ __forceinline__ float sigmoid_f32(float z) {
@@ -43,57 +52,89 @@ __device__ __forceinline__ float clamp_sym(float u, float L) {
     return (fabsf(u) > L) ? copysignf(L, u) : u;
 }
 
-template <int W, int G, int V>
-__global__ __launch_bounds__(kBlock) void swiglu_clamped_fwd_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ probs, uint16_t* __restrict__ y,
-    int64_t rows, int64_t inter, float L) {
-    constexpr int kGroups = kBlock / G;
-    const int lane = threadIdx.x & (G - 1);
-    const int64_t nvec = inter / W;
-    const int64_t row_step = static_cast<int64_t>(gridDim.x) * kGroups;
-    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kGroups + threadIdx.x / G; r < rows; r += row_step) {
+__device__ __forceinline__ float fwd_elem(float g, float u, float p, float L) {
+    const float gc = clamp_hi(g, L);
+    const float uc = clamp_sym(u, L);
+    const float s = sigmoid_f32(gc);
+    return ((gc * s) * uc) * p;
+}
+
+// d_gate, d_up for one element; adds this element's probability-gradient term
+// gy * silu(gc) * uc to acc when kGradProbs.
+template <bool kGradProbs>
+__device__ __forceinline__ void bwd_elem(float g, float u, float gy, float p, float L, float& dg, float& du,
+                                         float& acc) {
+    const float gc = clamp_hi(g, L);
+    const float uc = clamp_sym(u, L);
+    const float s = sigmoid_f32(gc);
+    const float a = gc * s;  // silu(gc)
+    const float t = gy * p;
+    if (kGradProbs) acc = __fmaf_rn(gy, a * uc, acc);
+    const float dsilu = s * (1.0f + gc * (1.0f - s));
+    dg = (g <= L) ? (t * uc) * dsilu : 0.0f;
+    du = (fabsf(u) <= L) ? t * a : 0.0f;
+}
+
+__device__ __forceinline__ u32x4 fwd_vec(u32x4 g, u32x4 u, float p, float L) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = pack_bf16x2(fwd_elem(bf16_lo(g[i]), bf16_lo(u[i]), p, L), fwd_elem(bf16_hi(g[i]), bf16_hi(u[i]), p, L));
+    return o;
+}
+
+template <bool kGradProbs>
+__device__ __forceinline__ void bwd_vec(u32x4 g, u32x4 u, u32x4 gy, float p, float L, u32x4& dg, u32x4& du,
+                                        float& acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float dg0, dg1, du0, du1;
+        bwd_elem<kGradProbs>(bf16_lo(g[i]), bf16_lo(u[i]), bf16_lo(gy[i]), p, L, dg0, du0, acc);
+        bwd_elem<kGradProbs>(bf16_hi(g[i]), bf16_hi(u[i]), bf16_hi(gy[i]), p, L, dg1, du1, acc);
+        dg[i] = pack_bf16x2(dg0, dg1);
+        du[i] = pack_bf16x2(du0, du1);
+    }
+}
+
+// ---- 16-byte vector kernels (inter % 8 == 0, 16-byte aligned tensors) ------
+
+template <int G, int V>
+__global__ __launch_bounds__(kFwdBlock) void swiglu_clamped_fwd_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ probs, uint16_t* __restrict__ y, int64_t rows,
+    int64_t inter, float L) {
+    constexpr int kRows = kFwdBlock / G;
+    const int lane = threadIdx.x % G;
+    const int64_t nvec = inter / 8;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kRows + threadIdx.x / G; r < rows;
+         r += static_cast<int64_t>(gridDim.x) * kRows) {
         const uint16_t* gate = x + r * 2 * inter;
         const uint16_t* up = gate + inter;
         uint16_t* yr = y + r * inter;
         const float p = probs[r];
         for (int64_t c0 = lane; c0 < nvec; c0 += static_cast<int64_t>(G) * V) {
-            float g[V][W], u[V][W];
+            u32x4 g[V], u[V];
 #pragma unroll
-            for (int k = 0; k < V; ++k) {
-                const int64_t c = c0 + static_cast<int64_t>(k) * G;
-                if (c < nvec) {
-                    Io<W>::load(gate + c * W, g[k]);
-                    Io<W>::load(up + c * W, u[k]);
-                }
-            }
+            for (int k = 0; k < V; ++k)
+                if (c0 + k * G < nvec) g[k] = load_stream(gate + (c0 + k * G) * 8);
 #pragma unroll
-            for (int k = 0; k < V; ++k) {
-                const int64_t c = c0 + static_cast<int64_t>(k) * G;
-                if (c < nvec) {
-                    float o[W];
+            for (int k = 0; k < V; ++k)
+                if (c0 + k * G < nvec) u[k] = load_stream(up + (c0 + k * G) * 8);
 #pragma unroll
-                    for (int e = 0; e < W; ++e) {
-                        const float gc = clamp_hi(g[k][e], L);
-                        const float uc = clamp_sym(u[k][e], L);
-                        const float s = sigmoid_f32(gc);
-                        o[e] = ((gc * s) * uc) * p;
-                    }
-                    Io<W>::store(yr + c * W, o);
-                }
-            }
+            for (int k = 0; k < V; ++k)
+                if (c0 + k * G < nvec) store_stream(yr + (c0 + k * G) * 8, fwd_vec(g[k], u[k], p, L));
         }
     }
 }
 
-template <int W, int G, int V, bool kGradProbs>
-__global__ __launch_bounds__(kBlock) void swiglu_clamped_bwd_kernel(
+template <int G, int V, bool kGradProbs>
+__global__ __launch_bounds__(kBwdBlock) void swiglu_clamped_bwd_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ probs, const uint16_t* __restrict__ grad_y,
     uint16_t* __restrict__ grad_x, float* __restrict__ grad_probs, int64_t rows, int64_t inter, float L) {
-    constexpr int kGroups = kBlock / G;
-    const int lane = threadIdx.x & (G - 1);
-    const int64_t nvec = inter / W;
-    const int64_t row_step = static_cast<int64_t>(gridDim.x) * kGroups;
-    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kGroups + threadIdx.x / G; r < rows; r += row_step) {
+    constexpr int kRows = kBwdBlock / G;
+    const int lane = threadIdx.x % G;
+    const int64_t nvec = inter / 8;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kRows + threadIdx.x / G; r < rows;
+         r += static_cast<int64_t>(gridDim.x) * kRows) {
         const uint16_t* gate = x + r * 2 * inter;
         const uint16_t* up = gate + inter;
         const uint16_t* gyr = grad_y + r * inter;
@@ -102,36 +143,23 @@ __global__ __launch_bounds__(kBlock) void swiglu_clamped_bwd_kernel(
         const float p = probs[r];
         float acc = 0.0f;
         for (int64_t c0 = lane; c0 < nvec; c0 += static_cast<int64_t>(G) * V) {
-            float g[V][W], u[V][W], gy[V][W];
+            u32x4 g[V], u[V], gy[V];
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                if (c0 + k * G < nvec) g[k] = load_stream(gate + (c0 + k * G) * 8);
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                if (c0 + k * G < nvec) u[k] = load_stream(up + (c0 + k * G) * 8);
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                if (c0 + k * G < nvec) gy[k] = load_stream(gyr + (c0 + k * G) * 8);
 #pragma unroll
             for (int k = 0; k < V; ++k) {
-                const int64_t c = c0 + static_cast<int64_t>(k) * G;
-                if (c < nvec) {
-                    Io<W>::load(gate + c * W, g[k]);
-                    Io<W>::load(up + c * W, u[k]);
-                    Io<W>::load(gyr + c * W, gy[k]);
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < V; ++k) {
-                const int64_t c = c0 + static_cast<int64_t>(k) * G;
-                if (c < nvec) {
-                    float dg[W], du[W];
-#pragma unroll
-                    for (int e = 0; e < W; ++e) {
-                        const float gv = g[k][e], uv = u[k][e];
-                        const float gc = clamp_hi(gv, L);
-                        const float uc = clamp_sym(uv, L);
-                        const float s = sigmoid_f32(gc);
-                        const float a = gc * s;                 // silu(gc)
-                        const float t = gy[k][e] * p;
-                        if (kGradProbs) acc = __fmaf_rn(gy[k][e], a * uc, acc);
-                        const float dsilu = s * (1.0f + gc * (1.0f - s));
-                        dg[e] = (gv <= L) ? (t * uc) * dsilu : 0.0f;
-                        du[e] = (fabsf(uv) <= L) ? t * a : 0.0f;
-                    }
-                    Io<W>::store(dgate + c * W, dg);
-                    Io<W>::store(dup + c * W, du);
+                if (c0 + k * G < nvec) {
+                    u32x4 dg, du;
+                    bwd_vec<kGradProbs>(g[k], u[k], gy[k], p, L, dg, du, acc);
+                    store_stream(dgate + (c0 + k * G) * 8, dg);
+                    store_stream(dup + (c0 + k * G) * 8, du);
                 }
             }
         }
@@ -142,53 +170,68 @@ __global__ __launch_bounds__(kBlock) void swiglu_clamped_bwd_kernel(
     }
 }
 
-// Lane-group width G and vectors per lane V for a row of nvec vectors.
-struct Shape {
-    int G, V;
-};
+// ---- per-element kernels (any inter, 2-byte aligned tensors) ---------------
 
-inline Shape pick_shape(int64_t nvec) {
-    if (nvec >= 64) {
-        int64_t v = (nvec + 63) / 64;
-        return Shape{64, static_cast<int>(v > 4 ? 4 : v)};
+__global__ __launch_bounds__(kFwdBlock) void swiglu_clamped_fwd_scalar_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ probs, uint16_t* __restrict__ y, int64_t rows,
+    int64_t inter, float L) {
+    constexpr int kRows = kFwdBlock / 64;
+    const int lane = threadIdx.x % 64;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kRows + threadIdx.x / 64; r < rows;
+         r += static_cast<int64_t>(gridDim.x) * kRows) {
+        const uint16_t* gate = x + r * 2 * inter;
+        const float p = probs[r];
+        for (int64_t j = lane; j < inter; j += 64)
+            y[r * inter + j] = to_bf16(fwd_elem(bf16_at(gate + j), bf16_at(gate + inter + j), p, L));
     }
-    if (nvec > 16) return Shape{32, 1};
-    if (nvec > 8) return Shape{16, 1};
-    return Shape{8, 1};
 }
 
-constexpr int64_t kMaxBlocks = 1 << 20;  // 2^28 work-items at most; the row loop strides over the rest
+template <bool kGradProbs>
+__global__ __launch_bounds__(kBwdBlock) void swiglu_clamped_bwd_scalar_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ probs, const uint16_t* __restrict__ grad_y,
+    uint16_t* __restrict__ grad_x, float* __restrict__ grad_probs, int64_t rows, int64_t inter, float L) {
+    constexpr int kRows = kBwdBlock / 64;
+    const int lane = threadIdx.x % 64;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kRows + threadIdx.x / 64; r < rows;
+         r += static_cast<int64_t>(gridDim.x) * kRows) {
+        const uint16_t* gate = x + r * 2 * inter;
+        uint16_t* dgate = grad_x + r * 2 * inter;
+        const float p = probs[r];
+        float acc = 0.0f;
+        for (int64_t j = lane; j < inter; j += 64) {
+            float dg, du;
+            bwd_elem<kGradProbs>(bf16_at(gate + j), bf16_at(gate + inter + j), bf16_at(grad_y + r * inter + j), p, L,
+                                 dg, du, acc);
+            dgate[j] = to_bf16(dg);
+            dgate[inter + j] = to_bf16(du);
+        }
+        if (kGradProbs) {
+            acc = group_sum<64>(acc);
+            if (lane == 0) grad_probs[r] = acc;
+        }
+    }
+}
 
-template <int W, int G, int V>
+// ---- launchers ---------------------------------------------------------------
+
+template <int G, int V>
 void launch_fwd(const uint16_t* x, const float* probs, uint16_t* y, int64_t rows, int64_t inter, float L,
                 hipStream_t st) {
-    const unsigned grid = grid_for_rows(rows, kBlock / G, kMaxBlocks);
-    hipLaunchKernelGGL((swiglu_clamped_fwd_kernel<W, G, V>), dim3(grid), dim3(kBlock), 0, st, x, probs, y, rows,
-                       inter, L);
+    hipLaunchKernelGGL((swiglu_clamped_fwd_kernel<G, V>), dim3(grid_for_rows(rows, kFwdBlock / G)),
+                       dim3(kFwdBlock), 0, st, x, probs, y, rows, inter, L);
 }
 
-template <int W, int G, int V>
+template <int G, int V>
 void launch_bwd(const uint16_t* x, const float* probs, const uint16_t* gy, uint16_t* gx, float* gp, int64_t rows,
                 int64_t inter, float L, hipStream_t st) {
-    const unsigned grid = grid_for_rows(rows, kBlock / G, kMaxBlocks);
+    const dim3 grid(grid_for_rows(rows, kBwdBlock / G));
     if (gp)
-        hipLaunchKernelGGL((swiglu_clamped_bwd_kernel<W, G, V, true>), dim3(grid), dim3(kBlock), 0, st, x, probs, gy,
-                           gx, gp, rows, inter, L);
+        hipLaunchKernelGGL((swiglu_clamped_bwd_kernel<G, V, true>), grid, dim3(kBwdBlock), 0, st, x, probs, gy, gx,
+                           gp, rows, inter, L);
     else
-        hipLaunchKernelGGL((swiglu_clamped_bwd_kernel<W, G, V, false>), dim3(grid), dim3(kBlock), 0, st, x, probs,
-                           gy, gx, gp, rows, inter, L);
+        hipLaunchKernelGGL((swiglu_clamped_bwd_kernel<G, V, false>), grid, dim3(kBwdBlock), 0, st, x, probs, gy,
+                           gx, gp, rows, inter, L);
 }
-
-#define MOE_EPI_DISPATCH_SHAPE(SHAPE, LAUNCH, ...)                          \
-    do {                                                                    \
-        if ((SHAPE).G == 64 && (SHAPE).V == 4) LAUNCH<8, 64, 4>(__VA_ARGS__); \
-        else if ((SHAPE).G == 64 && (SHAPE).V == 3) LAUNCH<8, 64, 3>(__VA_ARGS__); \
-        else if ((SHAPE).G == 64 && (SHAPE).V == 2) LAUNCH<8, 64, 2>(__VA_ARGS__); \
-        else if ((SHAPE).G == 64) LAUNCH<8, 64, 1>(__VA_ARGS__);            \
-        else if ((SHAPE).G == 32) LAUNCH<8, 32, 1>(__VA_ARGS__);            \
-        else if ((SHAPE).G == 16) LAUNCH<8, 16, 1>(__VA_ARGS__);            \
-        else LAUNCH<8, 8, 1>(__VA_ARGS__);                                  \
-    } while (0)
 
 // Common argument checks; returns MOE_EPI_SUCCESS and fills the byte sizes of
 // x / grad_x, of y / grad_y and of probs / grad_probs.
@@ -219,10 +262,11 @@ extern "C" int swiglu_clamped_fwd(const uint16_t* x, const float* probs, uint16_
     hipStream_t s = as_stream(stream);
     (void)hipGetLastError();
     if (inter % 8 == 0 && aligned(x, 16) && aligned(y, 16)) {
-        const Shape sh = pick_shape(inter / 8);
+        const Shape sh = pick_shape(inter / 8, kVmax);
         MOE_EPI_DISPATCH_SHAPE(sh, launch_fwd, x, probs, y, rows, inter, limit, s);
     } else {
-        launch_fwd<1, 64, 4>(x, probs, y, rows, inter, limit, s);
+        hipLaunchKernelGGL(swiglu_clamped_fwd_scalar_kernel, dim3(grid_for_rows(rows, kFwdBlock / 64)),
+                           dim3(kFwdBlock), 0, s, x, probs, y, rows, inter, limit);
     }
     return launch_status();
 }
@@ -247,10 +291,16 @@ extern "C" int swiglu_clamped_bwd(const uint16_t* x, const float* probs, const u
     hipStream_t s = as_stream(stream);
     (void)hipGetLastError();
     if (inter % 8 == 0 && aligned(x, 16) && aligned(grad_y, 16) && aligned(grad_x, 16)) {
-        const Shape sh = pick_shape(inter / 8);
+        const Shape sh = pick_shape(inter / 8, kVmax);
         MOE_EPI_DISPATCH_SHAPE(sh, launch_bwd, x, probs, grad_y, grad_x, grad_probs, rows, inter, limit, s);
     } else {
-        launch_bwd<1, 64, 4>(x, probs, grad_y, grad_x, grad_probs, rows, inter, limit, s);
+        const dim3 grid(grid_for_rows(rows, kBwdBlock / 64));
+        if (grad_probs)
+            hipLaunchKernelGGL(swiglu_clamped_bwd_scalar_kernel<true>, grid, dim3(kBwdBlock), 0, s, x, probs, grad_y,
+                               grad_x, grad_probs, rows, inter, limit);
+        else
+            hipLaunchKernelGGL(swiglu_clamped_bwd_scalar_kernel<false>, grid, dim3(kBwdBlock), 0, s, x, probs,
+                               grad_y, grad_x, grad_probs, rows, inter, limit);
     }
     return launch_status();
 }
