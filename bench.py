@@ -21,9 +21,13 @@ Prints one JSON line. Options:
   --workload NAME    swiglu_* or router_65536x7168 (router: fwd + bwd of the
                      fp32 router-weight multiply)
   --no-cpu-baseline  skip the oracle timing on the host
-  --copy-calibration time torch's device copy of 1 GiB instead (the plain copy
-                     kernel whose counter readings scale FETCH_SIZE/WRITE_SIZE)
+  --copy-calibration time a 1 GiB device-to-device copy instead (torch's copy_,
+                     carried out by the HIP runtime's copy kernel): the plain
+                     copy of known size whose FETCH_SIZE / WRITE_SIZE readings
+                     scale those counters for the kernels above
 """
+from __future__ import annotations
+
 import argparse
 import hashlib
 import json
@@ -67,17 +71,28 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, workload: str):
-    """HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
-    (scaled by the copy-kernel calibration), if taken on the current sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+PROFILE_FOR = {"swiglu": "swiglu_clamped", "router": "router_weight_mul"}
+
+
+def load_traffic(kernel: str, workload) -> float | None:
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary profiles/<op>_<rows>x<cols>.md (FETCH_SIZE and WRITE_SIZE, each
+    scaled by its reading for a device copy of known size). None if there is
+    no summary or it was taken on other kernel sources."""
+    name = f"{PROFILE_FOR[workload.op]}_{workload.rows}x{workload.cols}.md"
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
-    with open(path) as fh:
-        rec = json.load(fh)
+    text = open(path).read()
+    start = text.find("```json")
+    if start < 0:
+        return None
+    block = text[start + len("```json"):text.find("```", start + 7)]
+    rec = json.loads(block)
     if rec.get("kernel_source_digest") != kernel_source_digest():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
 
 
 def copy_calibration(args):
@@ -182,7 +197,7 @@ def main():
 
     kernels = {names[0]: kstats(names[0], fwd_b, fwd_ms), names[1]: kstats(names[1], bwd_b, bwd_ms)}
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
-    traffic = load_traffic(dom, w.name)
+    traffic = load_traffic(dom, w)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GB/s"], "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": kernels[dom]["GB/s"] / PEAK_HBM_GBS, "traffic": traffic,
                 "algorithmic_bytes_per_launch": kernels[dom]["algorithmic_bytes"]}

@@ -63,39 +63,61 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // A lane group of G lanes owns one row; each lane handles V vectors per pass
 // over the row. G = 64 (a wavefront per row) once a row has >= 64 vectors;
-// V is chosen so a row takes as few passes as possible with at most vmax
-// vectors per lane, and the last pass wastes as few lanes as possible.
+// V is the smallest instantiated count (1-8, 10, 12, 14, 16) that covers the
+// row in as few passes as possible with at most vmax vectors per lane.
 struct Shape {
     int G, V;
 };
+
+inline int round_up_instantiated(int64_t v) {
+    static const int kCounts[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16};
+    for (int c : kCounts)
+        if (v <= c) return c;
+    return 16;
+}
 
 inline Shape pick_shape(int64_t nvec, int vmax) {
     if (nvec >= 64) {
         const int64_t per_lane = (nvec + 63) / 64;
         const int64_t passes = (per_lane + vmax - 1) / vmax;
-        return Shape{64, static_cast<int>((per_lane + passes - 1) / passes)};
+        int v = round_up_instantiated((per_lane + passes - 1) / passes);
+        return Shape{64, v > vmax ? vmax : v};
     }
     if (nvec > 16) return Shape{32, 1};
     if (nvec > 8) return Shape{16, 1};
     return Shape{8, 1};
 }
 
-// Calls LAUNCH<G, V>(args...) for the shapes pick_shape can return.
-#define MOE_EPI_DISPATCH_SHAPE(SHAPE, LAUNCH, ...)                     \
-    do {                                                               \
-        switch ((SHAPE).G == 64 ? (SHAPE).V : -(SHAPE).G) {            \
-            case 1: LAUNCH<64, 1>(__VA_ARGS__); break;                 \
-            case 2: LAUNCH<64, 2>(__VA_ARGS__); break;                 \
-            case 3: LAUNCH<64, 3>(__VA_ARGS__); break;                 \
-            case 4: LAUNCH<64, 4>(__VA_ARGS__); break;                 \
-            case 5: LAUNCH<64, 5>(__VA_ARGS__); break;                 \
-            case 6: LAUNCH<64, 6>(__VA_ARGS__); break;                 \
-            case 7: LAUNCH<64, 7>(__VA_ARGS__); break;                 \
-            case 8: LAUNCH<64, 8>(__VA_ARGS__); break;                 \
-            case -32: LAUNCH<32, 1>(__VA_ARGS__); break;               \
-            case -16: LAUNCH<16, 1>(__VA_ARGS__); break;               \
-            default: LAUNCH<8, 1>(__VA_ARGS__); break;                 \
-        }                                                              \
+// Calls LAUNCH<G, V>(args...) for the shape picked with vmax = VMAX. Counts
+// above VMAX are not instantiated for that caller; should one ever be asked
+// for, VMAX vectors per pass are used instead (the kernels loop over passes,
+// so any V covers the row).
+#define MOE_EPI_CASE_V(VMAX, N, LAUNCH, ...)        \
+    case N:                                         \
+        if constexpr (N <= VMAX)                    \
+            LAUNCH<64, (N <= VMAX ? N : VMAX)>(__VA_ARGS__); \
+        else                                        \
+            LAUNCH<64, VMAX>(__VA_ARGS__);          \
+        break;
+#define MOE_EPI_DISPATCH_SHAPE(VMAX, SHAPE, LAUNCH, ...)                          \
+    do {                                                                          \
+        switch ((SHAPE).G == 64 ? (SHAPE).V : -(SHAPE).G) {                       \
+            MOE_EPI_CASE_V(VMAX, 1, LAUNCH, __VA_ARGS__)                          \
+            MOE_EPI_CASE_V(VMAX, 2, LAUNCH, __VA_ARGS__)                          \
+            MOE_EPI_CASE_V(VMAX, 3, LAUNCH, __VA_ARGS__)                          \
+            MOE_EPI_CASE_V(VMAX, 4, LAUNCH, __VA_ARGS__)                          \
+            MOE_EPI_CASE_V(VMAX, 5, LAUNCH, __VA_ARGS__)                          \
+            MOE_EPI_CASE_V(VMAX, 6, LAUNCH, __VA_ARGS__)                          \
+            MOE_EPI_CASE_V(VMAX, 7, LAUNCH, __VA_ARGS__)                          \
+            MOE_EPI_CASE_V(VMAX, 8, LAUNCH, __VA_ARGS__)                          \
+            MOE_EPI_CASE_V(VMAX, 10, LAUNCH, __VA_ARGS__)                         \
+            MOE_EPI_CASE_V(VMAX, 12, LAUNCH, __VA_ARGS__)                         \
+            MOE_EPI_CASE_V(VMAX, 14, LAUNCH, __VA_ARGS__)                         \
+            MOE_EPI_CASE_V(VMAX, 16, LAUNCH, __VA_ARGS__)                         \
+            case -32: LAUNCH<32, 1>(__VA_ARGS__); break;                          \
+            case -16: LAUNCH<16, 1>(__VA_ARGS__); break;                          \
+            default: LAUNCH<8, 1>(__VA_ARGS__); break;                            \
+        }                                                                         \
     } while (0)
 
 // Grid size for a row loop: one lane group per row, capped (a grid must stay

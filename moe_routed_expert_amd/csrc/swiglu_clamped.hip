@@ -263,7 +263,7 @@ extern "C" int swiglu_clamped_fwd(const uint16_t* x, const float* probs, uint16_
     (void)hipGetLastError();
     if (inter % 8 == 0 && aligned(x, 16) && aligned(y, 16)) {
         const Shape sh = pick_shape(inter / 8, kVmax);
-        MOE_EPI_DISPATCH_SHAPE(sh, launch_fwd, x, probs, y, rows, inter, limit, s);
+        MOE_EPI_DISPATCH_SHAPE(kVmax, sh, launch_fwd, x, probs, y, rows, inter, limit, s);
     } else {
         hipLaunchKernelGGL(swiglu_clamped_fwd_scalar_kernel, dim3(grid_for_rows(rows, kFwdBlock / 64)),
                            dim3(kFwdBlock), 0, s, x, probs, y, rows, inter, limit);
@@ -292,7 +292,7 @@ extern "C" int swiglu_clamped_bwd(const uint16_t* x, const float* probs, const u
     (void)hipGetLastError();
     if (inter % 8 == 0 && aligned(x, 16) && aligned(grad_y, 16) && aligned(grad_x, 16)) {
         const Shape sh = pick_shape(inter / 8, kVmax);
-        MOE_EPI_DISPATCH_SHAPE(sh, launch_bwd, x, probs, grad_y, grad_x, grad_probs, rows, inter, limit, s);
+        MOE_EPI_DISPATCH_SHAPE(kVmax, sh, launch_bwd, x, probs, grad_y, grad_x, grad_probs, rows, inter, limit, s);
     } else {
         const dim3 grid(grid_for_rows(rows, kBwdBlock / 64));
         if (grad_probs)
