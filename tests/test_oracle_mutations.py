@@ -1,0 +1,112 @@
+"""The pins catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a copy of oracle/oracle.c (a dropped term, a
+wrong sign, a swapped operand or half, an exclusive mask, a clamp on the wrong
+side, truncation instead of round-to-nearest-even, ...), builds it with the
+oracle's own flags in a temporary directory, loads it through a fresh copy of
+the oracle wrapper and runs the pin tests of tests/test_oracle_pins.py
+against it. At least one pin must fail for every planted mistake. The real
+oracle is never modified; everything here runs on the CPU.
+"""
+import importlib.util
+import os
+import subprocess
+
+import pytest
+
+import oracle as real_oracle
+from oracle import build as oracle_build
+from tests import test_oracle_pins as pins
+
+SRC = oracle_build.SRC
+
+# (name, text in oracle.c, replacement)
+MUTANTS = [
+    ("gate clamped from below too", "float gc = (g > L) ? L : g;",
+     "float gc = (g > L) ? L : ((g < -L) ? -L : g);"),
+    ("exclusive gate mask", "int mask_g = (g <= L);", "int mask_g = (g < L);"),
+    ("exclusive up mask", "int mask_u = (-L <= u) && (u <= L);", "int mask_u = (-L < u) && (u < L);"),
+    ("up clamped from above only", "float uc = (u > L) ? L : ((u < -L) ? -L : u);", "float uc = (u > L) ? L : u;"),
+    ("sigmoid sign", "float sig = 1.0f / (1.0f + expf(-gc));", "float sig = 1.0f / (1.0f + expf(gc));"),
+    ("silu of the unclamped gate", "float a = gc * sig;", "float a = g * sig;"),
+    ("silu' term dropped", "float dsilu = sig * (1.0f + gc * (1.0f - sig));", "float dsilu = sig;"),
+    ("silu' sign flipped", "float dsilu = sig * (1.0f + gc * (1.0f - sig));",
+     "float dsilu = sig * (1.0f - gc * (1.0f - sig));"),
+    ("d_gate without the probability", "out[1] = mask_g ? (t * uc) * dsilu : 0.0f;",
+     "out[1] = mask_g ? (gy * uc) * dsilu : 0.0f;"),
+    ("d_up with the wrong factor", "out[2] = mask_u ? t * a : 0.0f;", "out[2] = mask_u ? t * uc : 0.0f;"),
+    ("masked gradient as -0", "out[2] = mask_u ? t * a : 0.0f;", "out[2] = mask_u ? t * a : -0.0f;"),
+    ("probability-gradient term times p", "out[3] = gy * h;", "out[3] = gy * h * p;"),
+    ("forward without the probability", "out[0] = h * p;", "out[0] = h;"),
+    ("gate and up halves swapped (forward)",
+     "oracle_swiglu_point(oracle_bf16_to_f32(xr[j]), oracle_bf16_to_f32(xr[inter + j]),\n                                probs[r], 0.0f, L, q);",
+     "oracle_swiglu_point(oracle_bf16_to_f32(xr[inter + j]), oracle_bf16_to_f32(xr[j]),\n                                probs[r], 0.0f, L, q);"),
+    ("d_gate and d_up halves swapped", "gxr[j] = oracle_f32_to_bf16(q[1]);\n            gxr[inter + j] = oracle_f32_to_bf16(q[2]);",
+     "gxr[j] = oracle_f32_to_bf16(q[2]);\n            gxr[inter + j] = oracle_f32_to_bf16(q[1]);"),
+    ("truncation instead of rounding", "if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))", "if (0)"),
+    ("ties away from zero", "if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))", "if (dropped >= 0x8000u)"),
+    ("router grad_x from x", "grad_x[r * hidden + k] = oracle_f32_to_bf16(g * probs[r]);",
+     "grad_x[r * hidden + k] = oracle_f32_to_bf16(oracle_bf16_to_f32(x ? x[r * hidden + k] : grad_out[r * hidden + k]) * probs[r]);"),
+    ("router grad_probs squares grad_out", "float term = g * oracle_bf16_to_f32(x[r * hidden + k]);", "float term = g * g;"),
+    ("router forward skips the probability", "float v = oracle_bf16_to_f32(x[r * hidden + k]) * probs[r];",
+     "float v = oracle_bf16_to_f32(x[r * hidden + k]);"),
+    ("row sums in float32", "acc += (double)q[3];", "acc = (double)((float)acc + q[3]);"),
+]
+
+
+def _pins():
+    """Every pin test, with its parameters bound, cheapest first."""
+    calls = [
+        ("rounding via router forward", lambda o: pins.test_oracle_rounding_matches_torch_via_router_forward(o)),
+        ("hand-derived cases", lambda o: [pins.test_bwd_hand_derived_cases(c, o) for c in pins._golden_rows()]),
+        ("fwd gate sweep L=7", lambda o: pins.test_fwd_every_bf16_gate_vs_float64_library(7.0, o)),
+        ("fwd up sweep", lambda o: pins.test_fwd_every_bf16_up_vs_float64_library(o)),
+        ("bwd gate sweep", lambda o: pins.test_bwd_every_bf16_gate_vs_autograd(o)),
+        ("bwd up sweep", lambda o: pins.test_bwd_every_bf16_up_vs_autograd(o)),
+        ("one-sided differences", lambda o: pins.test_bwd_one_sided_differences_at_the_limits(o)),
+        ("cancellation in row sums", lambda o: pins.test_grad_probs_keep_small_terms_next_to_cancelling_large_ones(o)),
+        ("central differences", lambda o: pins.test_bwd_matches_central_finite_differences(o)),
+        ("brute force 4x8", lambda o: pins.test_bruteforce_4x8_dependency_structure(o)),
+        ("fwd workload", lambda o: pins.test_fwd_workload_vs_float64_library("swiglu_256x128", o)),
+        ("bwd workloads", lambda o: [pins.test_bwd_workload_vs_autograd(w, o) for w in
+                                     (pins.WORKLOADS["swiglu_256x128"],)]),
+        ("textbook swiglu", lambda o: pins.test_fwd_reduces_to_textbook_swiglu_without_clamp(o)),
+        ("router fwd eager", lambda o: pins.test_router_fwd_bitwise_equals_eager_fp32_multiply(o)),
+        ("router bwd exact", lambda o: pins.test_router_bwd_grad_x_bitwise_equals_eager_and_grad_probs_exact(o)),
+        ("router bwd without x", lambda o: pins.test_router_bwd_without_probability_gradient_skips_x(o)),
+        ("power-of-two scaling", lambda o: pins.test_power_of_two_scaling_is_exact(o)),
+    ]
+    return calls
+
+
+def _load_mutant(tmp_path, name, find, repl):
+    src = open(SRC).read()
+    assert src.count(find) >= 1, f"mutation '{name}' no longer matches oracle.c"
+    mutated = src.replace(find, repl, 1)
+    c_path = tmp_path / "oracle_mutant.c"
+    c_path.write_text(mutated)
+    so = tmp_path / "liboracle_mutant.so"
+    subprocess.run(["gcc", *oracle_build.CFLAGS, str(c_path), "-o", str(so), "-lm"], check=True)
+    spec = importlib.util.spec_from_file_location(f"oracle_mutant_{abs(hash(name))}",
+                                                  os.path.join(os.path.dirname(SRC), "__init__.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    mod._LIB_PATH = str(so)
+    mod._lib = None
+    return mod
+
+
+def test_the_real_oracle_passes_every_pin():
+    for label, call in _pins():
+        call(real_oracle)
+
+
+@pytest.mark.parametrize("name,find,repl", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_every_planted_mistake_is_caught(tmp_path, name, find, repl):
+    mod = _load_mutant(tmp_path, name, find, repl)
+    for label, call in _pins():
+        try:
+            call(mod)
+        except AssertionError:
+            return  # caught
+    pytest.fail(f"no pin catches the planted mistake: {name}")

@@ -26,7 +26,7 @@ import pytest
 import torch
 import torch.nn.functional as F
 
-import oracle
+import oracle as oracle_module
 from moe_routed_expert_amd.workloads import WORKLOADS, custom
 from tests.numerics import (bf16_bits_to_f32, bf16_is_nan, bf16_ulp_diff, f32_ulp,
                             f64_to_bf16_exact, fraction_to_f32)
@@ -57,6 +57,12 @@ def torch_swiglu_f64(gate, up, p, L, gy=None):
     return y.detach().numpy(), g.grad.numpy(), u.grad.numpy(), pp.grad.numpy()[:, 0]
 
 
+@pytest.fixture
+def o():
+    """The oracle under test (tests/test_oracle_mutations.py passes planted-mistake builds)."""
+    return oracle_module
+
+
 def split_gate_up(x_bits, inter):
     xf = bf16_bits_to_f32(x_bits).astype(np.float64)
     return xf[:, :inter], xf[:, inter:]
@@ -64,7 +70,7 @@ def split_gate_up(x_bits, inter):
 
 # ---- the test helpers themselves, against torch's conversions -------------
 
-def test_helper_exact_bf16_rounding_agrees_with_torch_on_f32_inputs():
+def test_helper_exact_bf16_rounding_agrees_with_torch_on_f32_inputs(o):
     rng = np.random.default_rng(11)
     bits = rng.integers(0, 2**32, size=400_000, dtype=np.uint64).astype(np.uint32)
     ties = ((rng.integers(0, 2**16, size=20_000).astype(np.uint32) << 16) | 0x8000).astype(np.uint32)
@@ -73,7 +79,7 @@ def test_helper_exact_bf16_rounding_agrees_with_torch_on_f32_inputs():
     assert np.array_equal(f64_to_bf16_exact(f.astype(np.float64)), torch_bf16_bits(f))
 
 
-def test_helper_fraction_rounding_agrees_with_hardware_conversion():
+def test_helper_fraction_rounding_agrees_with_hardware_conversion(o):
     rng = np.random.default_rng(12)
     d = np.concatenate([rng.standard_normal(2000) * 10.0 ** rng.integers(-40, 39, 2000),
                         rng.standard_normal(200) * 1e-42])
@@ -83,14 +89,14 @@ def test_helper_fraction_rounding_agrees_with_hardware_conversion():
 
 # ---- bfloat16 conversion inside the oracle ---------------------------------
 
-def test_oracle_widening_is_exact_for_every_pattern():
-    got = np.array([oracle.bf16_to_f32(int(b)) for b in ALL_BF16], dtype=np.float32)
+def test_oracle_widening_is_exact_for_every_pattern(o):
+    got = np.array([o.bf16_to_f32(int(b)) for b in ALL_BF16], dtype=np.float32)
     nan = np.isnan(ALL_F)
     assert np.array_equal(np.isnan(got), nan)
     assert np.array_equal(got[~nan].view(np.uint32), ALL_F[~nan].view(np.uint32))
 
 
-def test_oracle_rounding_matches_torch_via_router_forward():
+def test_oracle_rounding_matches_torch_via_router_forward(o):
     # router forward with x = 1.0 returns bf16(p): the oracle's rounding on
     # every p, including all tie patterns and values next to the overflow edge.
     rng = np.random.default_rng(13)
@@ -100,7 +106,7 @@ def test_oracle_rounding_matches_torch_via_router_forward():
                      0x80008000, 0x00007FFF, 0xFF7F8000], dtype=np.uint32)
     p = np.concatenate([bits, ties, edge]).view(np.float32)
     x = np.full((p.size, 1), 0x3F80, dtype=np.uint16)
-    out = oracle.router_weight_mul_fwd(x, p, p.size, 1)[:, 0]
+    out = o.router_weight_mul_fwd(x, p, p.size, 1)[:, 0]
     ref = torch_bf16_bits(p)
     nan = np.isnan(p)
     assert np.array_equal(out[~nan], ref[~nan])
@@ -109,20 +115,20 @@ def test_oracle_rounding_matches_torch_via_router_forward():
 
 # ---- clamped SwiGLU forward -------------------------------------------------
 
-def _sweep_fwd(gates, ups, p, L):
+def _sweep_fwd(o, gates, ups, p, L):
     n = gates.size
     inter = 256
     rows = n // inter
     x = np.concatenate([gates.reshape(rows, inter), ups.reshape(rows, inter)], axis=1)
     probs = np.full(rows, p, dtype=np.float32)
-    return oracle.swiglu_clamped_fwd(x, probs, rows, inter, L).ravel()
+    return o.swiglu_clamped_fwd(x, probs, rows, inter, L).ravel()
 
 
 @pytest.mark.parametrize("L", [7.0, 10.0])
-def test_fwd_every_bf16_gate_vs_float64_library(L):
+def test_fwd_every_bf16_gate_vs_float64_library(L, o):
     gates = ALL_BF16
     ups = np.full_like(gates, 0x3F80)                       # up = 1
-    y = _sweep_fwd(gates, ups, 1.0, L)
+    y = _sweep_fwd(o, gates, ups, 1.0, L)
     gf = ALL_F64
     ref64, *_ = torch_swiglu_f64(gf[None, :], np.ones((1, gf.size)), np.ones(1), L)
     ref = f64_to_bf16_exact(ref64[0])
@@ -136,12 +142,12 @@ def test_fwd_every_bf16_gate_vs_float64_library(L):
     assert np.all(np.abs(bf16_bits_to_f32(y[deep]).astype(np.float64) - ref64[0][deep]) <= 1e-30)
 
 
-def test_fwd_every_bf16_up_vs_float64_library():
+def test_fwd_every_bf16_up_vs_float64_library(o):
     L = 7.0
     ups = ALL_BF16
     gates = np.full_like(ups, 0x3FC0)                       # gate = 1.5
     p = np.float32(0.75)
-    y = _sweep_fwd(gates, ups, p, L)
+    y = _sweep_fwd(o, gates, ups, p, L)
     uf = ALL_F64
     ref64, *_ = torch_swiglu_f64(np.full((1, uf.size), 1.5), uf[None, :], np.array([0.75]), L)
     ref = f64_to_bf16_exact(ref64[0])
@@ -157,24 +163,24 @@ def test_fwd_every_bf16_up_vs_float64_library():
 
 
 @pytest.mark.parametrize("name", ["swiglu_256x128"])
-def test_fwd_workload_vs_float64_library(name):
+def test_fwd_workload_vs_float64_library(name, o):
     w = WORKLOADS[name]
     d = w.generate()
-    y = oracle.swiglu_clamped_fwd(d["x"], d["probs"], w.rows, w.cols, w.limit)
+    y = o.swiglu_clamped_fwd(d["x"], d["probs"], w.rows, w.cols, w.limit)
     g, u = split_gate_up(d["x"], w.cols)
     ref64, *_ = torch_swiglu_f64(g, u, d["probs"].astype(np.float64), w.limit)
     diff = bf16_ulp_diff(y, f64_to_bf16_exact(ref64))
     assert diff.max() <= 1 and (diff == 0).mean() > 0.995
 
 
-def test_fwd_reduces_to_textbook_swiglu_without_clamp():
+def test_fwd_reduces_to_textbook_swiglu_without_clamp(o):
     # With L beyond every input and p = 1 the method is silu(gate) * up.
     rng = np.random.default_rng(14)
     rows, inter = 64, 96
     gf = (rng.standard_normal((rows, inter)) * 6).astype(np.float32)
     uf = (rng.standard_normal((rows, inter)) * 6).astype(np.float32)
     x = np.concatenate([torch_bf16_bits(gf), torch_bf16_bits(uf)], axis=1)
-    y = oracle.swiglu_clamped_fwd(x, np.ones(rows, np.float32), rows, inter, 1e30)
+    y = o.swiglu_clamped_fwd(x, np.ones(rows, np.float32), rows, inter, 1e30)
     gt = torch.from_numpy(bf16_bits_to_f32(x[:, :inter]))
     ut = torch.from_numpy(bf16_bits_to_f32(x[:, inter:]))
     ref = (F.silu(gt) * ut).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
@@ -183,22 +189,22 @@ def test_fwd_reduces_to_textbook_swiglu_without_clamp():
 
 # ---- clamped SwiGLU backward -----------------------------------------------
 
-def _sweep_bwd(gates, ups, p, gy_bits, L):
+def _sweep_bwd(o, gates, ups, p, gy_bits, L):
     n = gates.size
     inter = 256
     rows = n // inter
     x = np.concatenate([gates.reshape(rows, inter), ups.reshape(rows, inter)], axis=1)
     probs = np.full(rows, p, dtype=np.float32)
-    gx, gp = oracle.swiglu_clamped_bwd(x, probs, gy_bits.reshape(rows, inter), rows, inter, L)
+    gx, gp = o.swiglu_clamped_bwd(x, probs, gy_bits.reshape(rows, inter), rows, inter, L)
     return gx[:, :inter].ravel(), gx[:, inter:].ravel(), gp
 
 
-def test_bwd_every_bf16_gate_vs_autograd():
+def test_bwd_every_bf16_gate_vs_autograd(o):
     L = 7.0
     gates = ALL_BF16
     ups = np.full_like(gates, 0x3FC0)                       # up = 1.5
     gy = np.full_like(gates, 0x3F80)                        # gy = 1
-    dg, du, _ = _sweep_bwd(gates, ups, 1.0, gy, L)
+    dg, du, _ = _sweep_bwd(o, gates, ups, 1.0, gy, L)
     gf = ALL_F64
     _, g_grad, u_grad, _ = torch_swiglu_f64(gf[None, :], np.full((1, gf.size), 1.5), np.ones(1), L,
                                             gy=np.ones((1, gf.size)))
@@ -213,12 +219,12 @@ def test_bwd_every_bf16_gate_vs_autograd():
     assert np.all(dg[ok & (gf < -L)] != 0)
 
 
-def test_bwd_every_bf16_up_vs_autograd():
+def test_bwd_every_bf16_up_vs_autograd(o):
     L = 7.0
     ups = ALL_BF16
     gates = np.full_like(ups, 0x3FC0)                       # gate = 1.5
     gy = np.full_like(ups, 0xBF40)                          # gy = -0.75
-    dg, du, _ = _sweep_bwd(gates, ups, 0.5, gy, L)
+    dg, du, _ = _sweep_bwd(o, gates, ups, 0.5, gy, L)
     uf = ALL_F64
     _, g_grad, u_grad, _ = torch_swiglu_f64(np.full((1, uf.size), 1.5), uf[None, :], np.array([0.5]), L,
                                             gy=np.full((1, uf.size), -0.75))
@@ -238,9 +244,9 @@ def test_bwd_every_bf16_up_vs_autograd():
            x_special_values=(-7.0, 7.0, 0.0, -7.03125, 7.03125, -6.96875, 6.96875),
            probs_kind="uniform_zeros", probs_zero_frac=0.2),
 ])
-def test_bwd_workload_vs_autograd(wl):
+def test_bwd_workload_vs_autograd(wl, o):
     d = wl.generate()
-    gx, gp = oracle.swiglu_clamped_bwd(d["x"], d["probs"], d["grad_out"], wl.rows, wl.cols, wl.limit)
+    gx, gp = o.swiglu_clamped_bwd(d["x"], d["probs"], d["grad_out"], wl.rows, wl.cols, wl.limit)
     g, u = split_gate_up(d["x"], wl.cols)
     gy = bf16_bits_to_f32(d["grad_out"]).astype(np.float64)
     _, g_grad, u_grad, p_grad = torch_swiglu_f64(g, u, d["probs"].astype(np.float64), wl.limit, gy=gy)
@@ -258,14 +264,14 @@ def test_bwd_workload_vs_autograd(wl):
     assert np.all(np.abs(gp.astype(np.float64) - p_grad) <= 1e-6 * scale + 1e-30)
 
 
-def test_bwd_zero_probability_rows():
+def test_bwd_zero_probability_rows(o):
     wl = WORKLOADS["swiglu_100003x1536"]
     d = wl.generate(rows=4096)
     rows = 4096
     zero = d["probs"] == 0
     assert 0.1 < zero.mean() < 0.3
-    y = oracle.swiglu_clamped_fwd(d["x"], d["probs"], rows, wl.cols, wl.limit)
-    gx, gp = oracle.swiglu_clamped_bwd(d["x"], d["probs"], d["grad_out"], rows, wl.cols, wl.limit)
+    y = o.swiglu_clamped_fwd(d["x"], d["probs"], rows, wl.cols, wl.limit)
+    gx, gp = o.swiglu_clamped_bwd(d["x"], d["probs"], d["grad_out"], rows, wl.cols, wl.limit)
     assert np.all(y[zero] & 0x7FFF == 0)                 # +-0
     assert np.all(gx[zero] & 0x7FFF == 0)
     assert np.all(gp[zero] != 0)                         # d_probs does not vanish with p
@@ -288,15 +294,15 @@ def _closed(expr):
 
 
 @pytest.mark.parametrize("case", _golden_rows(), ids=lambda f: f[0])
-def test_bwd_hand_derived_cases(case):
+def test_bwd_hand_derived_cases(case, o):
     name, L, g, u, p, gy = case[0], *map(float, case[1:6])
     expects = case[6:10]
-    q = oracle.swiglu_point(g, u, p, gy, L)
-    x = np.array([[oracle.f32_to_bf16(g), oracle.f32_to_bf16(u)]], dtype=np.uint16)
+    q = o.swiglu_point(g, u, p, gy, L)
+    x = np.array([[o.f32_to_bf16(g), o.f32_to_bf16(u)]], dtype=np.uint16)
     assert bf16_bits_to_f32(x)[0, 0] == np.float32(g) and bf16_bits_to_f32(x)[0, 1] == np.float32(u)
-    y = oracle.swiglu_clamped_fwd(x, np.array([p], np.float32), 1, 1, L)[0, 0]
-    gx, gp = oracle.swiglu_clamped_bwd(x, np.array([p], np.float32),
-                                       np.array([[oracle.f32_to_bf16(gy)]], np.uint16), 1, 1, L)
+    y = o.swiglu_clamped_fwd(x, np.array([p], np.float32), 1, 1, L)[0, 0]
+    gx, gp = o.swiglu_clamped_bwd(x, np.array([p], np.float32),
+                                       np.array([[o.f32_to_bf16(gy)]], np.uint16), 1, 1, L)
     got = [int(y), int(gx[0, 0]), int(gx[0, 1])]
     for want, have in zip(expects[:3], got):
         if want.startswith("0x"):
@@ -309,7 +315,7 @@ def test_bwd_hand_derived_cases(case):
     assert abs(float(gp[0]) - term) <= 4 * f32_ulp(term) + 1e-30
 
 
-def test_bwd_matches_central_finite_differences():
+def test_bwd_matches_central_finite_differences(o):
     # d/dg, d/du and d/dp of the oracle's own unrounded forward (gy = 1), at
     # random points away from the clamp kinks.
     rng = np.random.default_rng(15)
@@ -320,8 +326,8 @@ def test_bwd_matches_central_finite_differences():
         p = rng.uniform(0.05, 1.0)
         if abs(g - L) < 0.05 or abs(abs(u) - L) < 0.05:
             continue
-        _, dg, du, term = oracle.swiglu_point(g, u, p, 1.0, L)
-        f = lambda gg, uu, pp: oracle.swiglu_point(gg, uu, pp, 1.0, L)[0]
+        _, dg, du, term = o.swiglu_point(g, u, p, 1.0, L)
+        f = lambda gg, uu, pp: o.swiglu_point(gg, uu, pp, 1.0, L)[0]
         hg = hu = 1e-2
         fd_g = (f(g + hg, u, p) - f(g - hg, u, p)) / (2 * hg)
         fd_u = (f(g, u + hu, p) - f(g, u - hu, p)) / (2 * hu)
@@ -333,32 +339,51 @@ def test_bwd_matches_central_finite_differences():
     assert checked > 300
 
 
-def test_bwd_one_sided_differences_at_the_limits():
+def test_bwd_one_sided_differences_at_the_limits(o):
     # At exactly +-L the inclusive masks keep the derivative from inside the
     # interval; one step outside, the function is flat and the gradient is +0.
     L, p, h = 7.0, 0.5, 1e-3
-    f = lambda g, u: oracle.swiglu_point(g, u, p, 1.0, L)[0]
+    f = lambda g, u: o.swiglu_point(g, u, p, 1.0, L)[0]
     for u in (-3.0, 2.0, L, -L):
-        dg = oracle.swiglu_point(L, u, p, 1.0, L)[1]
+        dg = o.swiglu_point(L, u, p, 1.0, L)[1]
         inside = (f(L, u) - f(L - h, u)) / h
         assert abs(inside - dg) <= 5e-3 * abs(dg) + 1e-3
         assert (f(L + h, u) - f(L, u)) == 0.0
-        assert oracle.swiglu_point(7.03125, u, p, 1.0, L)[1] == 0.0
+        assert o.swiglu_point(7.03125, u, p, 1.0, L)[1] == 0.0
     for g in (-2.0, 0.5, 3.0, L):
-        du_hi = oracle.swiglu_point(g, L, p, 1.0, L)[2]
+        du_hi = o.swiglu_point(g, L, p, 1.0, L)[2]
         assert abs((f(g, L) - f(g, L - h)) / h - du_hi) <= 5e-3 * abs(du_hi) + 1e-3
-        du_lo = oracle.swiglu_point(g, -L, p, 1.0, L)[2]
+        du_lo = o.swiglu_point(g, -L, p, 1.0, L)[2]
         assert abs((f(g, -L + h) - f(g, -L)) / h - du_lo) <= 5e-3 * abs(du_lo) + 1e-3
-        assert oracle.swiglu_point(g, 7.03125, p, 1.0, L)[2] == 0.0
-        assert oracle.swiglu_point(g, -7.03125, p, 1.0, L)[2] == 0.0
+        assert o.swiglu_point(g, 7.03125, p, 1.0, L)[2] == 0.0
+        assert o.swiglu_point(g, -7.03125, p, 1.0, L)[2] == 0.0
     # below -L the gate is not clamped: the central difference is the gradient
     g = -8.0
-    dg = oracle.swiglu_point(g, 1.0, p, 1.0, L)[1]
+    dg = o.swiglu_point(g, 1.0, p, 1.0, L)[1]
     fd = (f(g + h, 1.0) - f(g - h, 1.0)) / (2 * h)
     assert dg != 0.0 and abs(fd - dg) <= 5e-3 * abs(dg) + 1e-4
 
 
-def test_bruteforce_4x8_dependency_structure():
+def test_grad_probs_keep_small_terms_next_to_cancelling_large_ones(o):
+    # One row: gate = up = L = 8192 gives the term +2^26 (exact), then 126
+    # elements with gate = up = 1 (term silu(1)), then up = -8192 gives -2^26.
+    # The large terms cancel exactly; a sum carried at float64 keeps the small
+    # ones (a float32 running sum would lose every one of them next to 2^26).
+    L, inter = 8192.0, 128
+    g = np.ones(inter, np.float32)
+    u = np.ones(inter, np.float32)
+    g[0] = g[-1] = 8192.0
+    u[0], u[-1] = 8192.0, -8192.0
+    x = np.concatenate([torch_bf16_bits(g), torch_bf16_bits(u)])[None, :]
+    gy = np.full((1, inter), 0x3F80, np.uint16)
+    _, gp = o.swiglu_clamped_bwd(x, np.ones(1, np.float32), gy, 1, inter, L)
+    _, _, _, p_grad = torch_swiglu_f64(g[None, :].astype(np.float64), u[None, :].astype(np.float64),
+                                       np.ones(1), L, gy=np.ones((1, inter)))
+    assert abs(p_grad[0] - 126 * (1.0 / (1.0 + math.exp(-1.0)))) < 1e-6
+    assert abs(float(gp[0]) - p_grad[0]) <= 1e-4, (gp[0], p_grad[0])
+
+
+def test_bruteforce_4x8_dependency_structure(o):
     # rows = 4, inter = 4 (x is 4 x 8). Change one input at a time to a very
     # different value and record which outputs move: y[r, j], d_gate[r, j] and
     # d_up[r, j] may depend only on x[r, j], x[r, 4 + j], p[r] (and gy[r, j]);
@@ -374,8 +399,8 @@ def test_bruteforce_4x8_dependency_structure():
     gy = torch_bf16_bits(rng.choice([1.0, -0.5, 2.0], size=(rows, inter)).astype(np.float32))
 
     def run(x_, p_, gy_):
-        y = oracle.swiglu_clamped_fwd(x_, p_, rows, inter, L)
-        gx, gp = oracle.swiglu_clamped_bwd(x_, p_, gy_, rows, inter, L)
+        y = o.swiglu_clamped_fwd(x_, p_, rows, inter, L)
+        gx, gp = o.swiglu_clamped_bwd(x_, p_, gy_, rows, inter, L)
         return y, gx, gp
 
     y0, gx0, gp0 = run(x, p, gy)
@@ -405,17 +430,17 @@ def test_bruteforce_4x8_dependency_structure():
     assert np.array_equal(gx0[:, inter:] & 0x7FFF == 0, (np.abs(up) > L) | (gate == 0))
 
 
-def test_power_of_two_scaling_is_exact():
+def test_power_of_two_scaling_is_exact(o):
     wl = WORKLOADS["swiglu_256x128"]
     d = wl.generate()
     rows, I, L = wl.rows, wl.cols, wl.limit
     gy2 = torch_bf16_bits(bf16_bits_to_f32(d["grad_out"]) * 2)
-    gx1, gp1 = oracle.swiglu_clamped_bwd(d["x"], d["probs"], d["grad_out"], rows, I, L)
-    gx2, gp2 = oracle.swiglu_clamped_bwd(d["x"], d["probs"], gy2, rows, I, L)
+    gx1, gp1 = o.swiglu_clamped_bwd(d["x"], d["probs"], d["grad_out"], rows, I, L)
+    gx2, gp2 = o.swiglu_clamped_bwd(d["x"], d["probs"], gy2, rows, I, L)
     assert np.array_equal(bf16_bits_to_f32(gx2), bf16_bits_to_f32(gx1) * 2)
     assert np.array_equal(gp2, gp1 * 2)
-    y1 = oracle.swiglu_clamped_fwd(d["x"], d["probs"], rows, I, L)
-    y2 = oracle.swiglu_clamped_fwd(d["x"], d["probs"] * 2, rows, I, L)
+    y1 = o.swiglu_clamped_fwd(d["x"], d["probs"], rows, I, L)
+    y2 = o.swiglu_clamped_fwd(d["x"], d["probs"] * 2, rows, I, L)
     assert np.array_equal(bf16_bits_to_f32(y2), bf16_bits_to_f32(y1) * 2)
 
 
@@ -426,19 +451,19 @@ def _router_inputs(rows, hidden, seed):
     return w.generate()
 
 
-def test_router_fwd_bitwise_equals_eager_fp32_multiply():
+def test_router_fwd_bitwise_equals_eager_fp32_multiply(o):
     # The pages: the forward is bitwise-identical to (x.float() * probs.float()).to(dtype).
     d = _router_inputs(96, 7168, 31)
-    out = oracle.router_weight_mul_fwd(d["x"], d["probs"], 96, 7168)
+    out = o.router_weight_mul_fwd(d["x"], d["probs"], 96, 7168)
     xt = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16)
     ref = (xt.float() * torch.from_numpy(d["probs"])[:, None]).to(torch.bfloat16)
     assert np.array_equal(out, ref.view(torch.int16).numpy().view(np.uint16))
 
 
-def test_router_bwd_grad_x_bitwise_equals_eager_and_grad_probs_exact():
+def test_router_bwd_grad_x_bitwise_equals_eager_and_grad_probs_exact(o):
     rows, hidden = 12, 7168
     d = _router_inputs(rows, hidden, 32)
-    gx, gp = oracle.router_weight_mul_bwd(d["grad_out"], d["x"], d["probs"], rows, hidden)
+    gx, gp = o.router_weight_mul_bwd(d["grad_out"], d["x"], d["probs"], rows, hidden)
     gt = torch.from_numpy(d["grad_out"].view(np.int16)).view(torch.bfloat16)
     ref = (gt.float() * torch.from_numpy(d["probs"])[:, None]).to(torch.bfloat16)
     assert np.array_equal(gx, ref.view(torch.int16).numpy().view(np.uint16))
@@ -461,18 +486,18 @@ def test_router_bwd_grad_x_bitwise_equals_eager_and_grad_probs_exact():
     assert np.all(np.abs(pt.grad.numpy()[:, 0] - gp) <= 1e-5 * scale)
 
 
-def test_router_bwd_without_probability_gradient_skips_x():
+def test_router_bwd_without_probability_gradient_skips_x(o):
     rows, hidden = 8, 512
     d = _router_inputs(rows, hidden, 33)
-    gx_a, gp_a = oracle.router_weight_mul_bwd(d["grad_out"], d["x"], d["probs"], rows, hidden)
-    gx_b, gp_b = oracle.router_weight_mul_bwd(d["grad_out"], None, d["probs"], rows, hidden,
+    gx_a, gp_a = o.router_weight_mul_bwd(d["grad_out"], d["x"], d["probs"], rows, hidden)
+    gx_b, gp_b = o.router_weight_mul_bwd(d["grad_out"], None, d["probs"], rows, hidden,
                                               want_grad_probs=False)
     assert gp_b is None and np.array_equal(gx_a, gx_b)
 
 
-def test_oracle_threads_do_not_change_results():
+def test_oracle_threads_do_not_change_results(o):
     wl = WORKLOADS["swiglu_256x128"]
     d = wl.generate()
-    a = oracle.swiglu_clamped_bwd(d["x"], d["probs"], d["grad_out"], wl.rows, wl.cols, wl.limit, threads=1)
-    b = oracle.swiglu_clamped_bwd(d["x"], d["probs"], d["grad_out"], wl.rows, wl.cols, wl.limit, threads=7)
+    a = o.swiglu_clamped_bwd(d["x"], d["probs"], d["grad_out"], wl.rows, wl.cols, wl.limit, threads=1)
+    b = o.swiglu_clamped_bwd(d["x"], d["probs"], d["grad_out"], wl.rows, wl.cols, wl.limit, threads=7)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
