@@ -59,66 +59,49 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Sum of v over the G lanes of each row group of a block. G <= 64: the lanes of
+// one wavefront (shuffles only). G > 64 (a multiple of 64): each wavefront's
+// shuffle sum goes to LDS (`part`, one slot per wavefront of the block) and
+// the row's partial sums are added in a fixed order, so the result does not
+// depend on timing. With G > 64 every thread of the block must make the call
+// (it holds two barriers).
+template <int G>
+__device__ __forceinline__ float row_sum(float v, float* part) {
+    if constexpr (G <= 64) {
+        return group_sum<G>(v);
+    } else {
+        v = group_sum<64>(v);
+        if ((threadIdx.x & 63) == 0) part[threadIdx.x / 64] = v;
+        __syncthreads();
+        const int first = (threadIdx.x / G) * (G / 64);
+        float s = 0.0f;
+#pragma unroll
+        for (int q = 0; q < G / 64; ++q) s += part[first + q];
+        __syncthreads();
+        return s;
+    }
+}
+
 // ---- launch shapes ------------------------------------------------------------
 
-// A lane group of G lanes owns one row; each lane handles V vectors per pass
-// over the row. G = 64 (a wavefront per row) once a row has >= 64 vectors;
-// V is the smallest instantiated count (1-8, 10, 12, 14, 16) that covers the
-// row in as few passes as possible with at most vmax vectors per lane.
+// A launch shape: G lanes own one row (G <= 64 within a wavefront, or 64*W
+// for W wavefronts per row), each lane handles V 16-byte vectors per pass over
+// the row (the kernels loop over passes, so any V covers any row), and blocks
+// have B threads (B / G rows per block).
 struct Shape {
-    int G, V;
+    int G, V, B;
 };
 
-inline int round_up_instantiated(int64_t v) {
-    static const int kCounts[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16};
-    for (int c : kCounts)
-        if (v <= c) return c;
-    return 16;
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline int pow2_ceil(int64_t v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
 }
 
-inline Shape pick_shape(int64_t nvec, int vmax) {
-    if (nvec >= 64) {
-        const int64_t per_lane = (nvec + 63) / 64;
-        const int64_t passes = (per_lane + vmax - 1) / vmax;
-        int v = round_up_instantiated((per_lane + passes - 1) / passes);
-        return Shape{64, v > vmax ? vmax : v};
-    }
-    if (nvec > 16) return Shape{32, 1};
-    if (nvec > 8) return Shape{16, 1};
-    return Shape{8, 1};
-}
-
-// Calls LAUNCH<G, V>(args...) for the shape picked with vmax = VMAX. Counts
-// above VMAX are not instantiated for that caller; should one ever be asked
-// for, VMAX vectors per pass are used instead (the kernels loop over passes,
-// so any V covers the row).
-#define MOE_EPI_CASE_V(VMAX, N, LAUNCH, ...)        \
-    case N:                                         \
-        if constexpr (N <= VMAX)                    \
-            LAUNCH<64, (N <= VMAX ? N : VMAX)>(__VA_ARGS__); \
-        else                                        \
-            LAUNCH<64, VMAX>(__VA_ARGS__);          \
-        break;
-#define MOE_EPI_DISPATCH_SHAPE(VMAX, SHAPE, LAUNCH, ...)                          \
-    do {                                                                          \
-        switch ((SHAPE).G == 64 ? (SHAPE).V : -(SHAPE).G) {                       \
-            MOE_EPI_CASE_V(VMAX, 1, LAUNCH, __VA_ARGS__)                          \
-            MOE_EPI_CASE_V(VMAX, 2, LAUNCH, __VA_ARGS__)                          \
-            MOE_EPI_CASE_V(VMAX, 3, LAUNCH, __VA_ARGS__)                          \
-            MOE_EPI_CASE_V(VMAX, 4, LAUNCH, __VA_ARGS__)                          \
-            MOE_EPI_CASE_V(VMAX, 5, LAUNCH, __VA_ARGS__)                          \
-            MOE_EPI_CASE_V(VMAX, 6, LAUNCH, __VA_ARGS__)                          \
-            MOE_EPI_CASE_V(VMAX, 7, LAUNCH, __VA_ARGS__)                          \
-            MOE_EPI_CASE_V(VMAX, 8, LAUNCH, __VA_ARGS__)                          \
-            MOE_EPI_CASE_V(VMAX, 10, LAUNCH, __VA_ARGS__)                         \
-            MOE_EPI_CASE_V(VMAX, 12, LAUNCH, __VA_ARGS__)                         \
-            MOE_EPI_CASE_V(VMAX, 14, LAUNCH, __VA_ARGS__)                         \
-            MOE_EPI_CASE_V(VMAX, 16, LAUNCH, __VA_ARGS__)                         \
-            case -32: LAUNCH<32, 1>(__VA_ARGS__); break;                          \
-            case -16: LAUNCH<16, 1>(__VA_ARGS__); break;                          \
-            default: LAUNCH<8, 1>(__VA_ARGS__); break;                            \
-        }                                                                         \
-    } while (0)
+// Lanes per row for rows narrower than a wavefront.
+inline int small_group(int64_t nvec) { return nvec > 16 ? 32 : (nvec > 8 ? 16 : 8); }
 
 // Grid size for a row loop: one lane group per row, capped (a grid must stay
 // below 2^32 work-items) so that larger inputs are covered by the row loop.

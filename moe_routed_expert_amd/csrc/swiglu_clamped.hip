@@ -11,18 +11,17 @@
 // masks on the input values.
 //
 // Kernel shape (MI355X-first, not the page's Triton tiling):
-//   * A lane group of G lanes owns one row (G = 64: a wavefront per row).
-//     Lane l handles 16-byte vectors l, l + G, ... of the row, so each
-//     wavefront-wide access is 1 KiB contiguous in gate, up, grad_y and the
-//     outputs. All V vectors of a pass are loaded (gate, then up, then grad_y)
-//     before any math, so 2V (forward) or 3V (backward) 16-byte loads per lane
-//     are in flight; with V = 4 at inter = 2048 one pass covers the row.
-//   * Blocks of 256 threads (forward) and 128 threads (backward), one row per
-//     wavefront: the shapes that sustained the most bandwidth on MI355X among
-//     64-512 thread blocks, persistent grids and register double-buffering
-//     across rows.
+//   * A group of G lanes owns one row. Lane l handles 16-byte vectors
+//     l, l + G, ... of the row, so each wavefront-wide access is 1 KiB
+//     contiguous in gate, up, grad_y and the outputs. All V vectors of a pass
+//     are loaded (gate, then up, then grad_y) before any math. At inter = 2048
+//     the forward spreads a row over 4 wavefronts (1 vector per lane) and the
+//     backward over 2 (2 vectors per lane): the shapes that sustained the most
+//     bandwidth on MI355X among 1-4 wavefronts per row, 64-1024 thread blocks,
+//     persistent grids and register double-buffering across rows.
 //   * The probability gradient is a per-lane fp32 register accumulator,
-//     reduced across the G lanes with cross-lane shuffles; no LDS.
+//     reduced with cross-lane shuffles within each wavefront and, when a row
+//     spans several wavefronts, through a few LDS slots in a fixed order.
 //   * Elementwise streaming work: no MFMA, no LDS tiles, each input byte read
 //     once and each output byte written once (nontemporal accesses).
 //   * Math per element: compare/select clamps (NaN passes through, as in
@@ -34,9 +33,9 @@
 namespace moe_epi {
 namespace {
 
+// block sizes of the per-element kernels
 constexpr int kFwdBlock = 256;
 constexpr int kBwdBlock = 128;
-constexpr int kVmax = 4;
 
 // sigma(z) = 1 / (1 + e^-z) with e^-z = 2^(-z * log2(e)).
 __device__ __forceinline__ float sigmoid_f32(float z) {
@@ -97,16 +96,23 @@ __device__ __forceinline__ void bwd_vec(u32x4 g, u32x4 u, u32x4 gy, float p, flo
 }
 
 // ---- 16-byte vector kernels (inter % 8 == 0, 16-byte aligned tensors) ------
+//
+// G lanes own a row (G <= 64: part of a wavefront; G = 64*W: W wavefronts),
+// B threads per block, B / G rows per block. The row loop advances whole
+// blocks, so every thread of a block runs the same iterations (row_sum may
+// hold a barrier).
 
-template <int G, int V>
-__global__ __launch_bounds__(kFwdBlock) void swiglu_clamped_fwd_kernel(
+template <int G, int V, int B>
+__global__ __launch_bounds__(B) void swiglu_clamped_fwd_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ probs, uint16_t* __restrict__ y, int64_t rows,
     int64_t inter, float L) {
-    constexpr int kRows = kFwdBlock / G;
+    constexpr int kRows = B / G;
     const int lane = threadIdx.x % G;
     const int64_t nvec = inter / 8;
-    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kRows + threadIdx.x / G; r < rows;
-         r += static_cast<int64_t>(gridDim.x) * kRows) {
+    for (int64_t rb = static_cast<int64_t>(blockIdx.x) * kRows; rb < rows;
+         rb += static_cast<int64_t>(gridDim.x) * kRows) {
+        const int64_t r = rb + threadIdx.x / G;
+        if (r >= rows) continue;
         const uint16_t* gate = x + r * 2 * inter;
         const uint16_t* up = gate + inter;
         uint16_t* yr = y + r * inter;
@@ -126,46 +132,50 @@ __global__ __launch_bounds__(kFwdBlock) void swiglu_clamped_fwd_kernel(
     }
 }
 
-template <int G, int V, bool kGradProbs>
-__global__ __launch_bounds__(kBwdBlock) void swiglu_clamped_bwd_kernel(
+template <int G, int V, int B, bool kGradProbs>
+__global__ __launch_bounds__(B) void swiglu_clamped_bwd_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ probs, const uint16_t* __restrict__ grad_y,
     uint16_t* __restrict__ grad_x, float* __restrict__ grad_probs, int64_t rows, int64_t inter, float L) {
-    constexpr int kRows = kBwdBlock / G;
+    constexpr int kRows = B / G;
+    __shared__ float part[B / 64 > 0 ? B / 64 : 1];
     const int lane = threadIdx.x % G;
     const int64_t nvec = inter / 8;
-    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kRows + threadIdx.x / G; r < rows;
-         r += static_cast<int64_t>(gridDim.x) * kRows) {
-        const uint16_t* gate = x + r * 2 * inter;
-        const uint16_t* up = gate + inter;
-        const uint16_t* gyr = grad_y + r * inter;
-        uint16_t* dgate = grad_x + r * 2 * inter;
-        uint16_t* dup = dgate + inter;
-        const float p = probs[r];
+    for (int64_t rb = static_cast<int64_t>(blockIdx.x) * kRows; rb < rows;
+         rb += static_cast<int64_t>(gridDim.x) * kRows) {
+        const int64_t r = rb + threadIdx.x / G;
         float acc = 0.0f;
-        for (int64_t c0 = lane; c0 < nvec; c0 += static_cast<int64_t>(G) * V) {
-            u32x4 g[V], u[V], gy[V];
+        if (r < rows) {
+            const uint16_t* gate = x + r * 2 * inter;
+            const uint16_t* up = gate + inter;
+            const uint16_t* gyr = grad_y + r * inter;
+            uint16_t* dgate = grad_x + r * 2 * inter;
+            uint16_t* dup = dgate + inter;
+            const float p = probs[r];
+            for (int64_t c0 = lane; c0 < nvec; c0 += static_cast<int64_t>(G) * V) {
+                u32x4 g[V], u[V], gy[V];
 #pragma unroll
-            for (int k = 0; k < V; ++k)
-                if (c0 + k * G < nvec) g[k] = load_stream(gate + (c0 + k * G) * 8);
+                for (int k = 0; k < V; ++k)
+                    if (c0 + k * G < nvec) g[k] = load_stream(gate + (c0 + k * G) * 8);
 #pragma unroll
-            for (int k = 0; k < V; ++k)
-                if (c0 + k * G < nvec) u[k] = load_stream(up + (c0 + k * G) * 8);
+                for (int k = 0; k < V; ++k)
+                    if (c0 + k * G < nvec) u[k] = load_stream(up + (c0 + k * G) * 8);
 #pragma unroll
-            for (int k = 0; k < V; ++k)
-                if (c0 + k * G < nvec) gy[k] = load_stream(gyr + (c0 + k * G) * 8);
+                for (int k = 0; k < V; ++k)
+                    if (c0 + k * G < nvec) gy[k] = load_stream(gyr + (c0 + k * G) * 8);
 #pragma unroll
-            for (int k = 0; k < V; ++k) {
-                if (c0 + k * G < nvec) {
-                    u32x4 dg, du;
-                    bwd_vec<kGradProbs>(g[k], u[k], gy[k], p, L, dg, du, acc);
-                    store_stream(dgate + (c0 + k * G) * 8, dg);
-                    store_stream(dup + (c0 + k * G) * 8, du);
+                for (int k = 0; k < V; ++k) {
+                    if (c0 + k * G < nvec) {
+                        u32x4 dg, du;
+                        bwd_vec<kGradProbs>(g[k], u[k], gy[k], p, L, dg, du, acc);
+                        store_stream(dgate + (c0 + k * G) * 8, dg);
+                        store_stream(dup + (c0 + k * G) * 8, du);
+                    }
                 }
             }
         }
-        if (kGradProbs) {
-            acc = group_sum<G>(acc);
-            if (lane == 0) grad_probs[r] = acc;
+        if constexpr (kGradProbs) {
+            acc = row_sum<G>(acc, part);
+            if (lane == 0 && r < rows) grad_probs[r] = acc;
         }
     }
 }
@@ -213,24 +223,82 @@ __global__ __launch_bounds__(kBwdBlock) void swiglu_clamped_bwd_scalar_kernel(
 }
 
 // ---- launchers ---------------------------------------------------------------
+//
+// Shapes (measured on MI355X at 131072 x 2048; nontemporal 16-byte accesses):
+//   forward:  one vector per lane (V = 1) and up to 4 wavefronts per row,
+//             256-thread blocks (inter = 2048: 4 wavefronts, one row per block);
+//   backward: two vectors per lane (V = 2) and as many wavefronts per row as
+//             that needs (up to 8), two rows per block (inter = 2048: 2
+//             wavefronts per row, 256-thread blocks). Splitting a row over
+//             several wavefronts issues its loads from several SIMDs at once;
+//             these shapes ran 1-1.5% faster than one wavefront per row.
+//   Rows longer than the shape covers take several passes (V is capped).
 
-template <int G, int V>
+template <int G, int V, int B>
 void launch_fwd(const uint16_t* x, const float* probs, uint16_t* y, int64_t rows, int64_t inter, float L,
                 hipStream_t st) {
-    hipLaunchKernelGGL((swiglu_clamped_fwd_kernel<G, V>), dim3(grid_for_rows(rows, kFwdBlock / G)),
-                       dim3(kFwdBlock), 0, st, x, probs, y, rows, inter, L);
+    hipLaunchKernelGGL((swiglu_clamped_fwd_kernel<G, V, B>), dim3(grid_for_rows(rows, B / G)), dim3(B), 0, st, x,
+                       probs, y, rows, inter, L);
 }
 
-template <int G, int V>
+template <int G, int V, int B>
 void launch_bwd(const uint16_t* x, const float* probs, const uint16_t* gy, uint16_t* gx, float* gp, int64_t rows,
                 int64_t inter, float L, hipStream_t st) {
-    const dim3 grid(grid_for_rows(rows, kBwdBlock / G));
+    const dim3 grid(grid_for_rows(rows, B / G));
     if (gp)
-        hipLaunchKernelGGL((swiglu_clamped_bwd_kernel<G, V, true>), grid, dim3(kBwdBlock), 0, st, x, probs, gy, gx,
-                           gp, rows, inter, L);
+        hipLaunchKernelGGL((swiglu_clamped_bwd_kernel<G, V, B, true>), grid, dim3(B), 0, st, x, probs, gy, gx, gp,
+                           rows, inter, L);
     else
-        hipLaunchKernelGGL((swiglu_clamped_bwd_kernel<G, V, false>), grid, dim3(kBwdBlock), 0, st, x, probs, gy,
-                           gx, gp, rows, inter, L);
+        hipLaunchKernelGGL((swiglu_clamped_bwd_kernel<G, V, B, false>), grid, dim3(B), 0, st, x, probs, gy, gx, gp,
+                           rows, inter, L);
+}
+
+Shape fwd_shape(int64_t nvec) {
+    if (nvec < 64) return Shape{small_group(nvec), 1, 256};
+    const int w = pow2_ceil(ceil_div(nvec, 64)) > 4 ? 4 : pow2_ceil(ceil_div(nvec, 64));
+    const int64_t v = ceil_div(nvec, 64 * w);
+    return Shape{64 * w, static_cast<int>(v > 4 ? 4 : v), 256};
+}
+
+Shape bwd_shape(int64_t nvec) {
+    if (nvec < 64) return Shape{small_group(nvec), 1, 128};
+    if (nvec <= 128) return Shape{64, static_cast<int>(ceil_div(nvec, 64)), 128};
+    const int w = pow2_ceil(ceil_div(nvec, 128)) > 8 ? 8 : pow2_ceil(ceil_div(nvec, 128));
+    const int64_t v = ceil_div(nvec, 64 * w);
+    return Shape{64 * w, static_cast<int>(v > 4 ? 4 : v), 2 * 64 * w > 1024 ? 1024 : 2 * 64 * w};
+}
+
+void dispatch_fwd(const uint16_t* x, const float* probs, uint16_t* y, int64_t rows, int64_t inter, float L,
+                  hipStream_t st) {
+    const Shape sh = fwd_shape(inter / 8);
+    switch (sh.G * 8 + sh.V) {
+        case 8 * 8 + 1: return launch_fwd<8, 1, 256>(x, probs, y, rows, inter, L, st);
+        case 16 * 8 + 1: return launch_fwd<16, 1, 256>(x, probs, y, rows, inter, L, st);
+        case 32 * 8 + 1: return launch_fwd<32, 1, 256>(x, probs, y, rows, inter, L, st);
+        case 64 * 8 + 1: return launch_fwd<64, 1, 256>(x, probs, y, rows, inter, L, st);
+        case 128 * 8 + 1: return launch_fwd<128, 1, 256>(x, probs, y, rows, inter, L, st);
+        case 256 * 8 + 1: return launch_fwd<256, 1, 256>(x, probs, y, rows, inter, L, st);
+        case 256 * 8 + 2: return launch_fwd<256, 2, 256>(x, probs, y, rows, inter, L, st);
+        case 256 * 8 + 3: return launch_fwd<256, 3, 256>(x, probs, y, rows, inter, L, st);
+        default: return launch_fwd<256, 4, 256>(x, probs, y, rows, inter, L, st);
+    }
+}
+
+void dispatch_bwd(const uint16_t* x, const float* probs, const uint16_t* gy, uint16_t* gx, float* gp, int64_t rows,
+                  int64_t inter, float L, hipStream_t st) {
+    const Shape sh = bwd_shape(inter / 8);
+    switch (sh.G * 8 + sh.V) {
+        case 8 * 8 + 1: return launch_bwd<8, 1, 128>(x, probs, gy, gx, gp, rows, inter, L, st);
+        case 16 * 8 + 1: return launch_bwd<16, 1, 128>(x, probs, gy, gx, gp, rows, inter, L, st);
+        case 32 * 8 + 1: return launch_bwd<32, 1, 128>(x, probs, gy, gx, gp, rows, inter, L, st);
+        case 64 * 8 + 1: return launch_bwd<64, 1, 128>(x, probs, gy, gx, gp, rows, inter, L, st);
+        case 64 * 8 + 2: return launch_bwd<64, 2, 128>(x, probs, gy, gx, gp, rows, inter, L, st);
+        case 128 * 8 + 2: return launch_bwd<128, 2, 256>(x, probs, gy, gx, gp, rows, inter, L, st);
+        case 256 * 8 + 2: return launch_bwd<256, 2, 512>(x, probs, gy, gx, gp, rows, inter, L, st);
+        case 512 * 8 + 2: return launch_bwd<512, 2, 1024>(x, probs, gy, gx, gp, rows, inter, L, st);
+        case 512 * 8 + 3: return launch_bwd<512, 3, 1024>(x, probs, gy, gx, gp, rows, inter, L, st);
+        default: return launch_bwd<512, 4, 1024>(x, probs, gy, gx, gp, rows, inter, L, st);
+    }
 }
 
 // Common argument checks; returns MOE_EPI_SUCCESS and fills the byte sizes of
@@ -262,8 +330,7 @@ extern "C" int swiglu_clamped_fwd(const uint16_t* x, const float* probs, uint16_
     hipStream_t s = as_stream(stream);
     (void)hipGetLastError();
     if (inter % 8 == 0 && aligned(x, 16) && aligned(y, 16)) {
-        const Shape sh = pick_shape(inter / 8, kVmax);
-        MOE_EPI_DISPATCH_SHAPE(kVmax, sh, launch_fwd, x, probs, y, rows, inter, limit, s);
+        dispatch_fwd(x, probs, y, rows, inter, limit, s);
     } else {
         hipLaunchKernelGGL(swiglu_clamped_fwd_scalar_kernel, dim3(grid_for_rows(rows, kFwdBlock / 64)),
                            dim3(kFwdBlock), 0, s, x, probs, y, rows, inter, limit);
@@ -291,8 +358,7 @@ extern "C" int swiglu_clamped_bwd(const uint16_t* x, const float* probs, const u
     hipStream_t s = as_stream(stream);
     (void)hipGetLastError();
     if (inter % 8 == 0 && aligned(x, 16) && aligned(grad_y, 16) && aligned(grad_x, 16)) {
-        const Shape sh = pick_shape(inter / 8, kVmax);
-        MOE_EPI_DISPATCH_SHAPE(kVmax, sh, launch_bwd, x, probs, grad_y, grad_x, grad_probs, rows, inter, limit, s);
+        dispatch_bwd(x, probs, grad_y, grad_x, grad_probs, rows, inter, limit, s);
     } else {
         const dim3 grid(grid_for_rows(rows, kBwdBlock / 64));
         if (grad_probs)
