@@ -161,3 +161,98 @@ def router_weight_mul_bwd(grad_out, x, probs, rows, hidden, want_grad_probs=True
     if with_abs_sum:
         return grad_x, grad_probs, abs_sum
     return grad_x, grad_probs
+
+
+# ---- float16 / float32 storage --------------------------------------------
+
+BF16, F16, F32 = 0, 1, 2
+_NP = {BF16: np.uint16, F16: np.float16, F32: np.float32}
+
+
+def _typed_lib():
+    lib = _load()
+    if not getattr(lib, "_typed_ready", False):
+        vp = ctypes.c_void_p
+        lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_to_f32.restype = ctypes.c_float
+        lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+        lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+        lib.oracle_swiglu_clamped_fwd_typed.argtypes = [vp, ctypes.c_int, _f32p, vp, _i64, _i64, ctypes.c_float,
+                                                        ctypes.c_int]
+        lib.oracle_swiglu_clamped_bwd_typed.argtypes = [vp, ctypes.c_int, _f32p, vp, vp, _f32p, _f64p, _i64, _i64,
+                                                        ctypes.c_float, ctypes.c_int]
+        lib.oracle_router_weight_mul_fwd_typed.argtypes = [vp, ctypes.c_int, _f32p, vp, ctypes.c_int, _i64, _i64,
+                                                           ctypes.c_int]
+        lib.oracle_router_weight_mul_bwd_typed.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, _f32p, vp, _f32p,
+                                                           _f64p, _i64, _i64, ctypes.c_int]
+        for n in ("oracle_swiglu_clamped_fwd_typed", "oracle_swiglu_clamped_bwd_typed",
+                  "oracle_router_weight_mul_fwd_typed", "oracle_router_weight_mul_bwd_typed"):
+            getattr(lib, n).restype = None
+        lib._typed_ready = True
+    return lib
+
+
+def f16_to_f32(h: int) -> float:
+    return float(_typed_lib().oracle_f16_to_f32(int(h)))
+
+
+def f32_to_f16(f: float) -> int:
+    return int(_typed_lib().oracle_f32_to_f16(float(f)))
+
+
+def _vp(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def swiglu_clamped_fwd_typed(x, dtype, probs, rows, inter, L, threads=None):
+    """y ([rows, inter], same dtype as x). bf16 arrays are uint16 bit patterns."""
+    x = _arr(x, _NP[dtype], (rows, 2 * inter))
+    probs = _arr(probs, np.float32, (rows,))
+    y = np.empty((rows, inter), dtype=_NP[dtype])
+    _typed_lib().oracle_swiglu_clamped_fwd_typed(_vp(x), dtype, _p(probs, ctypes.c_float), _vp(y), rows, inter,
+                                                 float(L), threads or default_threads())
+    return y
+
+
+def swiglu_clamped_bwd_typed(x, dtype, probs, grad_y, rows, inter, L, want_grad_probs=True, threads=None,
+                             with_abs_sum=False):
+    """(grad_x, grad_probs or None[, abs_sum]) with grad_x of x's dtype."""
+    x = _arr(x, _NP[dtype], (rows, 2 * inter))
+    probs = _arr(probs, np.float32, (rows,))
+    grad_y = _arr(grad_y, _NP[dtype], (rows, inter))
+    grad_x = np.empty((rows, 2 * inter), dtype=_NP[dtype])
+    grad_probs = np.empty((rows,), dtype=np.float32) if want_grad_probs else None
+    abs_sum = np.empty((rows,), dtype=np.float64) if with_abs_sum else None
+    _typed_lib().oracle_swiglu_clamped_bwd_typed(_vp(x), dtype, _p(probs, ctypes.c_float), _vp(grad_y), _vp(grad_x),
+                                                 _p(grad_probs, ctypes.c_float), _p(abs_sum, ctypes.c_double),
+                                                 rows, inter, float(L), threads or default_threads())
+    if with_abs_sum:
+        return grad_x, grad_probs, abs_sum
+    return grad_x, grad_probs
+
+
+def router_weight_mul_fwd_typed(x, x_dtype, probs, out_dtype, rows, hidden, threads=None):
+    x = _arr(x, _NP[x_dtype], (rows, hidden))
+    probs = _arr(probs, np.float32, (rows,))
+    out = np.empty((rows, hidden), dtype=_NP[out_dtype])
+    _typed_lib().oracle_router_weight_mul_fwd_typed(_vp(x), x_dtype, _p(probs, ctypes.c_float), _vp(out), out_dtype,
+                                                    rows, hidden, threads or default_threads())
+    return out
+
+
+def router_weight_mul_bwd_typed(grad_out, go_dtype, x, x_dtype, probs, rows, hidden, want_grad_probs=True,
+                                threads=None, with_abs_sum=False):
+    """(grad_x of x_dtype, grad_probs or None[, abs_sum]); x may be None without grad_probs."""
+    grad_out = _arr(grad_out, _NP[go_dtype], (rows, hidden))
+    x = _arr(x, _NP[x_dtype], (rows, hidden)) if want_grad_probs else None
+    probs = _arr(probs, np.float32, (rows,))
+    grad_x = np.empty((rows, hidden), dtype=_NP[x_dtype])
+    grad_probs = np.empty((rows,), dtype=np.float32) if want_grad_probs else None
+    abs_sum = np.empty((rows,), dtype=np.float64) if (with_abs_sum and want_grad_probs) else None
+    _typed_lib().oracle_router_weight_mul_bwd_typed(_vp(grad_out), go_dtype, _vp(x), x_dtype,
+                                                    _p(probs, ctypes.c_float), _vp(grad_x),
+                                                    _p(grad_probs, ctypes.c_float), _p(abs_sum, ctypes.c_double),
+                                                    rows, hidden, threads or default_threads())
+    if with_abs_sum:
+        return grad_x, grad_probs, abs_sum
+    return grad_x, grad_probs

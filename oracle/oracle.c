@@ -206,3 +206,171 @@ void oracle_router_weight_mul_bwd(const uint16_t *grad_out, const uint16_t *x, c
             grad_probs_abs[r] = acc_abs;
     }
 }
+
+/* ---- other storage dtypes: float16 and float32 ------------------------ */
+/*
+ * [SW] lists bfloat16, float16 and float32 as the supported dtypes of x (the
+ * _SUPPORTED_DTYPES entry); [RW] lets the router multiply's output be the
+ * activation dtype or float32 (the out_dtype parameter of
+ * _RouterWeightMulFunction.forward, "fp32 for the scatter-add reduction
+ * path"). The math is the same binary32 chain; only loading and the final
+ * rounding depend on the dtype. Codes: 0 bfloat16, 1 float16, 2 float32.
+ */
+enum { ORACLE_BF16 = 0, ORACLE_F16 = 1, ORACLE_F32 = 2 };
+
+/* float16 -> binary32, exact: sign, 5-bit exponent (bias 15), 10-bit fraction. */
+float oracle_f16_to_f32(uint16_t h)
+{
+    uint32_t sign = (uint32_t)(h >> 15) << 31;
+    int ex = (h >> 10) & 0x1F;
+    uint32_t frac = h & 0x3FFu;
+    float mag;
+    if (ex == 0) {
+        mag = ldexpf((float)frac, -24);                 /* zero or subnormal: frac * 2^-24 */
+    } else if (ex == 31) {
+        uint32_t bits = 0x7F800000u | (frac << 13);     /* inf, or NaN keeping its payload */
+        memcpy(&mag, &bits, sizeof mag);
+    } else {
+        mag = ldexpf((float)(1024u + frac), ex - 25);   /* (1 + frac/1024) * 2^(ex-15) */
+    }
+    uint32_t bits;
+    memcpy(&bits, &mag, sizeof bits);
+    bits |= sign;
+    memcpy(&mag, &bits, sizeof mag);
+    return mag;
+}
+
+/* binary32 -> float16, to nearest, ties to even, with subnormals, overflow
+ * to infinity and NaN kept NaN (quiet bit set). The magnitude is written as an
+ * integer multiple n of the float16 unit in the last place at its exponent,
+ * and the dropped bits decide the rounding as for bfloat16. */
+uint16_t oracle_f32_to_f16(float f)
+{
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    uint16_t sign = (uint16_t)((bits >> 16) & 0x8000u);
+    int ef = (int)((bits >> 23) & 0xFFu);
+    uint32_t frac = bits & 0x7FFFFFu;
+    if (ef == 0xFF)
+        return (uint16_t)(sign | (frac ? (0x7E00u | (frac >> 13)) : 0x7C00u));
+    if (ef == 0)
+        return sign;                                     /* binary32 zero/subnormal: below half of 2^-24 */
+    int e = ef - 127;                                    /* value = m * 2^(e - 23), m in [2^23, 2^24) */
+    uint64_t m = (uint64_t)frac | 0x800000u;
+    int emin = e < -14 ? -14 : e;                        /* float16 exponent used (subnormals: -14) */
+    int sh = (emin - 10) - (e - 23);                     /* value / ulp = m / 2^sh, sh >= 13 */
+    uint64_t n, rem, half;
+    if (sh >= 40) {
+        n = 0; rem = m; half = (uint64_t)1 << 39;       /* m < 2^24: far below half an ulp */
+    } else {
+        n = m >> sh;
+        rem = m & (((uint64_t)1 << sh) - 1);
+        half = (uint64_t)1 << (sh - 1);
+    }
+    if (rem > half || (rem == half && (n & 1u)))
+        n += 1;
+    if (e < -14)
+        return (uint16_t)(sign | n);                     /* subnormal (n == 1024 is the smallest normal) */
+    uint32_t out = ((uint32_t)(e + 15) << 10) + (uint32_t)(n - 1024); /* n == 2048 carries into the exponent */
+    if (out >= 0x7C00u)
+        return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | out);
+}
+
+static float oracle_load(const void *p, int64_t i, int dtype)
+{
+    if (dtype == ORACLE_BF16)
+        return oracle_bf16_to_f32(((const uint16_t *)p)[i]);
+    if (dtype == ORACLE_F16)
+        return oracle_f16_to_f32(((const uint16_t *)p)[i]);
+    return ((const float *)p)[i];
+}
+
+static void oracle_store(void *p, int64_t i, int dtype, float v)
+{
+    if (dtype == ORACLE_BF16)
+        ((uint16_t *)p)[i] = oracle_f32_to_bf16(v);
+    else if (dtype == ORACLE_F16)
+        ((uint16_t *)p)[i] = oracle_f32_to_f16(v);
+    else
+        ((float *)p)[i] = v;
+}
+
+/* [SW] forward with x and y of one dtype. */
+void oracle_swiglu_clamped_fwd_typed(const void *x, int dtype, const float *probs, void *y,
+                                     int64_t rows, int64_t inter, float L, int nthreads)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (r = 0; r < rows; ++r) {
+        for (int64_t j = 0; j < inter; ++j) {
+            float q[4];
+            oracle_swiglu_point(oracle_load(x, r * 2 * inter + j, dtype),
+                                oracle_load(x, r * 2 * inter + inter + j, dtype), probs[r], 0.0f, L, q);
+            oracle_store(y, r * inter + j, dtype, q[0]);
+        }
+    }
+}
+
+/* [SW] backward with x, grad_y and grad_x of one dtype (grad_probs float32). */
+void oracle_swiglu_clamped_bwd_typed(const void *x, int dtype, const float *probs, const void *grad_y,
+                                     void *grad_x, float *grad_probs, double *grad_probs_abs,
+                                     int64_t rows, int64_t inter, float L, int nthreads)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (r = 0; r < rows; ++r) {
+        double acc = 0.0, acc_abs = 0.0;
+        for (int64_t j = 0; j < inter; ++j) {
+            float q[4];
+            oracle_swiglu_point(oracle_load(x, r * 2 * inter + j, dtype),
+                                oracle_load(x, r * 2 * inter + inter + j, dtype), probs[r],
+                                oracle_load(grad_y, r * inter + j, dtype), L, q);
+            oracle_store(grad_x, r * 2 * inter + j, dtype, q[1]);
+            oracle_store(grad_x, r * 2 * inter + inter + j, dtype, q[2]);
+            acc += (double)q[3];
+            acc_abs += fabs((double)q[3]);
+        }
+        if (grad_probs)
+            grad_probs[r] = (float)acc;
+        if (grad_probs_abs)
+            grad_probs_abs[r] = acc_abs;
+    }
+}
+
+/* [RW] forward: out (out_dtype) = round(fp32(x) * p); x of x_dtype. */
+void oracle_router_weight_mul_fwd_typed(const void *x, int x_dtype, const float *probs, void *out,
+                                        int out_dtype, int64_t rows, int64_t hidden, int nthreads)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < hidden; ++k)
+            oracle_store(out, r * hidden + k, out_dtype, oracle_load(x, r * hidden + k, x_dtype) * probs[r]);
+}
+
+/* [RW] backward: grad_out has the output's dtype, grad_x the dtype of x;
+ * grad_probs (float32) sums the binary32 products grad_out * x in binary64. */
+void oracle_router_weight_mul_bwd_typed(const void *grad_out, int go_dtype, const void *x, int x_dtype,
+                                        const float *probs, void *grad_x, float *grad_probs,
+                                        double *grad_probs_abs, int64_t rows, int64_t hidden, int nthreads)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (r = 0; r < rows; ++r) {
+        double acc = 0.0, acc_abs = 0.0;
+        for (int64_t k = 0; k < hidden; ++k) {
+            float g = oracle_load(grad_out, r * hidden + k, go_dtype);
+            oracle_store(grad_x, r * hidden + k, x_dtype, g * probs[r]);
+            if (grad_probs) {
+                float term = g * oracle_load(x, r * hidden + k, x_dtype);
+                acc += (double)term;
+                acc_abs += fabs((double)term);
+            }
+        }
+        if (grad_probs)
+            grad_probs[r] = (float)acc;
+        if (grad_probs && grad_probs_abs)
+            grad_probs_abs[r] = acc_abs;
+    }
+}

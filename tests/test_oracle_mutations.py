@@ -17,6 +17,7 @@ import pytest
 import oracle as real_oracle
 from oracle import build as oracle_build
 from tests import test_oracle_pins as pins
+from tests import test_oracle_pins_dtypes as dpins
 
 SRC = oracle_build.SRC
 
@@ -51,6 +52,17 @@ MUTANTS = [
     ("router forward skips the probability", "float v = oracle_bf16_to_f32(x[r * hidden + k]) * probs[r];",
      "float v = oracle_bf16_to_f32(x[r * hidden + k]);"),
     ("row sums in float32", "acc += (double)q[3];", "acc = (double)((float)acc + q[3]);"),
+    ("float16 truncation", "if (rem > half || (rem == half && (n & 1u)))", "if (0)"),
+    ("float16 ties away from zero", "if (rem > half || (rem == half && (n & 1u)))", "if (rem >= half)"),
+    ("float16 exponent bias", "uint32_t out = ((uint32_t)(e + 15) << 10)", "uint32_t out = ((uint32_t)(e + 16) << 10)"),
+    ("float16 subnormals flushed", "if (e < -14)\n        return (uint16_t)(sign | n);",
+     "if (e < -14)\n        return sign;"),
+    ("float16 widening bias", "mag = ldexpf((float)(1024u + frac), ex - 25);", "mag = ldexpf((float)(1024u + frac), ex - 24);"),
+    ("typed router forward skips the probability",
+     "oracle_store(out, r * hidden + k, out_dtype, oracle_load(x, r * hidden + k, x_dtype) * probs[r]);",
+     "oracle_store(out, r * hidden + k, out_dtype, oracle_load(x, r * hidden + k, x_dtype));"),
+    ("typed backward reads grad_y as x's neighbour",
+     "oracle_load(grad_y, r * inter + j, dtype), L, q);", "oracle_load(x, r * inter + j, dtype), L, q);"),
 ]
 
 
@@ -75,6 +87,15 @@ def _pins():
         ("router bwd exact", lambda o: pins.test_router_bwd_grad_x_bitwise_equals_eager_and_grad_probs_exact(o)),
         ("router bwd without x", lambda o: pins.test_router_bwd_without_probability_gradient_skips_x(o)),
         ("power-of-two scaling", lambda o: pins.test_power_of_two_scaling_is_exact(o)),
+        ("float16 widening", lambda o: dpins.test_f16_widening_every_pattern_matches_numpy(o)),
+        ("float16 rounding", lambda o: dpins.test_f16_rounding_matches_numpy_via_router_forward(o)),
+        ("typed bf16 = bf16", lambda o: dpins.test_typed_bf16_equals_untyped(o)),
+        ("float16 sweeps", lambda o: [dpins.test_f16_every_pattern_vs_float64_autograd(w, o) for w in ("gate", "up")]),
+        ("float32 bounds", lambda o: dpins.test_f32_random_inputs_within_derived_bounds(o)),
+        ("router dtypes fwd", lambda o: [dpins.test_router_typed_forward_bitwise_equals_eager(a, b, o)
+                                         for a, b in ((real_oracle.BF16, real_oracle.F32),
+                                                      (real_oracle.F16, real_oracle.F16))]),
+        ("router fp32 grad_out", lambda o: dpins.test_router_typed_backward_fp32_grad_out(o)),
     ]
     return calls
 
