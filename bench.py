@@ -20,6 +20,10 @@ Prints one JSON line. Options:
   --warmup W         untimed steps first (default 10)
   --workload NAME    swiglu_* or router_65536x7168 (router: fwd + bwd of the
                      fp32 router-weight multiply)
+  --dtype D          storage dtype of x / y / gradients: bf16 (default), f16, f32
+  --out-dtype D      router output (and grad_out) dtype: the x dtype or f32
+  --no-grad-probs    backward without the probability gradient (probabilities
+                     that carry no gradient; the router then does not read x)
   --no-cpu-baseline  skip the oracle timing on the host
   --copy-calibration time a 1 GiB device-to-device copy instead (torch's copy_,
                      carried out by the HIP runtime's copy kernel): the plain
@@ -52,6 +56,9 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--dtype", default="bf16", choices=("bf16", "f16", "f32"))
+    ap.add_argument("--out-dtype", default=None, choices=("bf16", "f16", "f32"))
+    ap.add_argument("--no-grad-probs", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=None)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -140,29 +147,38 @@ def main():
         return copy_calibration(args)
 
     w = WORKLOADS[args.workload or HEADLINE]
+    dt = args.dtype
+    od = (args.out_dtype or dt) if w.op == "router" else dt
+    want_gp = not args.no_grad_probs
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
-    d = w.generate()
-    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    print(f"[bench] generating {w.name} ({dt}{'' if od == dt else ' -> ' + od})", file=sys.stderr, flush=True)
+    d = w.generate(dtype=dt, grad_dtype=od)
+
+    def upload(a, kind):
+        if kind == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    x = upload(d["x"], dt)
     p = torch.from_numpy(d["probs"]).to(dev)
-    gy = torch.from_numpy(d["grad_out"].view(np.int16)).view(torch.bfloat16).to(dev)
+    gy = upload(d["grad_out"], od)
     rows, cols = w.rows, w.cols
+    gp = torch.empty((rows,), dtype=torch.float32, device=dev) if want_gp else None
     if w.op == "swiglu":
-        y = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((rows, cols), dtype=tdt[dt], device=dev)
         gx = torch.empty_like(x)
-        gp = torch.empty((rows,), dtype=torch.float32, device=dev)
         names = ("swiglu_clamped_fwd", "swiglu_clamped_bwd")
         fwd = lambda: epi.swiglu_clamped_fwd(x, p, y, w.limit)
         bwd = lambda: epi.swiglu_clamped_bwd(x, p, gy, gx, gp, w.limit)
     else:
-        out = torch.empty_like(x)
+        out = torch.empty((rows, cols), dtype=tdt[od], device=dev)
         gx = torch.empty_like(x)
-        gp = torch.empty((rows,), dtype=torch.float32, device=dev)
         names = ("router_weight_mul_fwd", "router_weight_mul_bwd")
         fwd = lambda: epi.router_weight_mul_fwd(x, p, out)
-        bwd = lambda: epi.router_weight_mul_bwd(gy, x, p, gx, gp)
-    fwd_b, bwd_b = w.fwd_bytes(), w.bwd_bytes()
+        bwd = lambda: epi.router_weight_mul_bwd(gy, x if want_gp else None, p, gx, gp)
+    fwd_b, bwd_b = w.fwd_bytes(dt, od), w.bwd_bytes(want_gp, dt, od)
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -196,8 +212,14 @@ def main():
                 "algorithmic_bytes": nbytes, "GB/s": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS}
 
     kernels = {names[0]: kstats(names[0], fwd_b, fwd_ms), names[1]: kstats(names[1], bwd_b, bwd_ms)}
+    # Counter traffic is taken for the bf16, with-gradient launch only.
+    variant = []
+    if dt != "bf16" or od != dt:
+        variant.append(f"{dt} storage" + ("" if od == dt else f", {od} output"))
+    if not want_gp:
+        variant.append("no probability gradient")
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
-    traffic = load_traffic(dom, w)
+    traffic = load_traffic(dom, w) if not variant else None
     roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GB/s"], "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": kernels[dom]["GB/s"] / PEAK_HBM_GBS, "traffic": traffic,
                 "algorithmic_bytes_per_launch": kernels[dom]["algorithmic_bytes"]}
@@ -206,20 +228,25 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         threads = args.cpu_threads or oracle.default_threads()
+        code = {"bf16": oracle.BF16, "f16": oracle.F16, "f32": oracle.F32}
         print(f"[bench] oracle on the host ({threads} threads), whole workload", file=sys.stderr, flush=True)
         t = time.perf_counter()
         if w.op == "swiglu":
-            oracle.swiglu_clamped_fwd(d["x"], d["probs"], rows, cols, w.limit, threads=threads)
-            oracle.swiglu_clamped_bwd(d["x"], d["probs"], d["grad_out"], rows, cols, w.limit, threads=threads)
+            oracle.swiglu_clamped_fwd_typed(d["x"], code[dt], d["probs"], rows, cols, w.limit, threads=threads)
+            oracle.swiglu_clamped_bwd_typed(d["x"], code[dt], d["probs"], d["grad_out"], rows, cols, w.limit,
+                                            want_grad_probs=want_gp, threads=threads)
         else:
-            oracle.router_weight_mul_fwd(d["x"], d["probs"], rows, cols, threads=threads)
-            oracle.router_weight_mul_bwd(d["grad_out"], d["x"], d["probs"], rows, cols, threads=threads)
+            oracle.router_weight_mul_fwd_typed(d["x"], code[dt], d["probs"], code[od], rows, cols, threads=threads)
+            oracle.router_weight_mul_bwd_typed(d["grad_out"], code[od], d["x"], code[dt], d["probs"], rows, cols,
+                                               want_grad_probs=want_gp, threads=threads)
         ct = time.perf_counter() - t
         cpu = {"value": (fwd_b + bwd_b) / ct / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
                "sample": f"the whole workload ({rows} rows), forward + backward once, {ct:.2f} s"}
 
+    headline = w.name == HEADLINE and not variant
     line = {
-        "metric": METRICS[w.op] if w.name == HEADLINE or w.op == "router" else METRICS["swiglu"] + f" ({w.name})",
+        "metric": METRICS[w.op] if headline or (w.op == "router" and not variant) else
+        METRICS[w.op] + f" ({w.name}{', ' if variant else ''}{', '.join(variant)})",
         "value": value,
         "unit": "GB/s",
         "n_gpus": 1,
@@ -233,8 +260,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "op": w.op, "rows": rows,
                    ("inter" if w.op == "swiglu" else "hidden"): cols,
-                   "limit": w.limit, "io": "bf16 tensors, fp32 probs; fp32 arithmetic",
-                   "bytes_per_step": fwd_b + bwd_b},
+                   "limit": w.limit, "storage": dt, "output": od, "grad_probs": want_gp,
+                   "io": f"{dt} tensors, fp32 probs; fp32 arithmetic", "bytes_per_step": fwd_b + bwd_b},
         "frac_of_peak": value / PEAK_HBM_GBS,
         "kernels": kernels,
         "roofline": roofline,

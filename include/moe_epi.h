@@ -44,8 +44,16 @@ typedef enum moe_epi_status {
     MOE_EPI_ERR_BAD_LIMIT = 3,    /* limit is not finite or not > 0                          */
     MOE_EPI_ERR_ALIAS = 4,        /* an output overlaps an input or another output           */
     MOE_EPI_ERR_MISALIGNED = 5,   /* a pointer is not aligned to its element size            */
-    MOE_EPI_ERR_LAUNCH = 6        /* the HIP runtime reported an error at kernel launch      */
+    MOE_EPI_ERR_LAUNCH = 6,       /* the HIP runtime reported an error at kernel launch      */
+    MOE_EPI_ERR_BAD_DTYPE = 7     /* a dtype code is not one of moe_epi_dtype                */
 } moe_epi_status;
+
+/* Storage types of the *_typed entry points. Arithmetic is float32 for all. */
+typedef enum moe_epi_dtype {
+    MOE_EPI_BF16 = 0,
+    MOE_EPI_F16 = 1,
+    MOE_EPI_F32 = 2
+} moe_epi_dtype;
 
 /*
  * Clamped SwiGLU times routing probability, forward.
@@ -118,6 +126,36 @@ int router_weight_mul_fwd(const uint16_t *x, const float *probs, uint16_t *out,
 int router_weight_mul_bwd(const uint16_t *grad_out, const uint16_t *x, const float *probs,
                           uint16_t *grad_x, float *grad_probs,
                           int64_t rows, int64_t hidden, void *stream);
+
+/*
+ * The same four operations for float16 and float32 storage.
+ * Page "nemo_automodel.components.moe.swiglu_triton" lists bfloat16, float16
+ * and float32 as the dtypes x may have (_SUPPORTED_DTYPES); page
+ * "nemo_automodel.components.moe.optimized_ops" lets the router multiply's
+ * output be the activation dtype or float32, the latter for combining expert
+ * outputs by scatter-add (out_dtype of _RouterWeightMulFunction.forward).
+ * Contract as above, with:
+ *   swiglu_clamped_*_typed: x, y, grad_y, grad_x all of `dtype`; each result
+ *     is rounded once from float32 to `dtype` (float32: stored as computed).
+ *   router_weight_mul_fwd_typed: x of `x_dtype`, out of `out_dtype`.
+ *   router_weight_mul_bwd_typed: grad_out of `grad_out_dtype` (the output's
+ *     dtype), x and grad_x of `x_dtype`; grad_probs float32.
+ * Pointers are typed void* (elements of the given dtypes); alignment is the
+ * element size, and the 16-byte path needs 16-byte aligned tensors and a row
+ * width that is a multiple of 8. A dtype outside moe_epi_dtype returns
+ * MOE_EPI_ERR_BAD_DTYPE. With every dtype MOE_EPI_BF16 these are exactly the
+ * calls above.
+ */
+int swiglu_clamped_fwd_typed(const void *x, const float *probs, void *y, int64_t rows, int64_t inter,
+                             float limit, int dtype, void *stream);
+int swiglu_clamped_bwd_typed(const void *x, const float *probs, const void *grad_y, void *grad_x,
+                             float *grad_probs, int64_t rows, int64_t inter, float limit, int dtype,
+                             void *stream);
+int router_weight_mul_fwd_typed(const void *x, int x_dtype, const float *probs, void *out, int out_dtype,
+                                int64_t rows, int64_t hidden, void *stream);
+int router_weight_mul_bwd_typed(const void *grad_out, int grad_out_dtype, const void *x, int x_dtype,
+                                const float *probs, void *grad_x, float *grad_probs, int64_t rows,
+                                int64_t hidden, void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *moe_epi_status_string(int status);

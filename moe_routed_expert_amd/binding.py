@@ -33,7 +33,11 @@ STATUS = {
     4: "MOE_EPI_ERR_ALIAS",
     5: "MOE_EPI_ERR_MISALIGNED",
     6: "MOE_EPI_ERR_LAUNCH",
+    7: "MOE_EPI_ERR_BAD_DTYPE",
 }
+
+# moe_epi_dtype codes of the *_typed entry points
+DTYPE_CODE = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
 
 _lib = None
 
@@ -58,7 +62,14 @@ def lib() -> ctypes.CDLL:
     L.swiglu_clamped_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, vp]
     L.router_weight_mul_fwd.argtypes = [vp, vp, vp, i64, i64, vp]
     L.router_weight_mul_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp]
-    for name in ("swiglu_clamped_fwd", "swiglu_clamped_bwd", "router_weight_mul_fwd", "router_weight_mul_bwd"):
+    i32 = ctypes.c_int
+    L.swiglu_clamped_fwd_typed.argtypes = [vp, vp, vp, i64, i64, f32, i32, vp]
+    L.swiglu_clamped_bwd_typed.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp]
+    L.router_weight_mul_fwd_typed.argtypes = [vp, i32, vp, vp, i32, i64, i64, vp]
+    L.router_weight_mul_bwd_typed.argtypes = [vp, i32, vp, i32, vp, vp, vp, i64, i64, vp]
+    for name in ("swiglu_clamped_fwd", "swiglu_clamped_bwd", "router_weight_mul_fwd", "router_weight_mul_bwd",
+                 "swiglu_clamped_fwd_typed", "swiglu_clamped_bwd_typed", "router_weight_mul_fwd_typed",
+                 "router_weight_mul_bwd_typed"):
         getattr(L, name).restype = ctypes.c_int
     L.moe_epi_status_string.argtypes = [ctypes.c_int]
     L.moe_epi_status_string.restype = ctypes.c_char_p
@@ -98,6 +109,12 @@ def _ptr(t: torch.Tensor | None):
     return None if t is None else t.data_ptr()
 
 
+def _code(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in DTYPE_CODE:
+        raise TypeError(f"{name}: expected bfloat16, float16 or float32, got {t.dtype}")
+    return DTYPE_CODE[t.dtype]
+
+
 def _rows_cols(x: torch.Tensor, name: str):
     if x.dim() != 2:
         raise ValueError(f"{name} must be 2-D, got {tuple(x.shape)}")
@@ -107,73 +124,98 @@ def _rows_cols(x: torch.Tensor, name: str):
 # ---- C-ABI entry points -----------------------------------------------------
 
 def swiglu_clamped_fwd(x, probs, y, limit: float, stream=None) -> None:
-    """y[:] = bf16(silu(min(gate, L)) * clamp(up, -L, L) * probs); x = [gate | up] bf16
-    [rows, 2*inter]; probs fp32 [rows] or [rows, 1]; y bf16 [rows, inter]."""
+    """y[:] = silu(min(gate, L)) * clamp(up, -L, L) * probs, rounded to x's dtype;
+    x = [gate | up] [rows, 2*inter] (bf16, fp16 or fp32); probs fp32 [rows] or
+    [rows, 1]; y [rows, inter] of x's dtype."""
     rows, two_i = _rows_cols(x, "x")
     if two_i % 2:
         raise ValueError("x must have an even number of columns ([gate | up])")
-    inter, dev = two_i // 2, x.device
-    _need(x, "x", torch.bfloat16, [(rows, two_i)], dev)
+    inter, dev, code = two_i // 2, x.device, _code(x, "x")
+    _need(x, "x", x.dtype, [(rows, two_i)], dev)
     _need(probs, "probs", torch.float32, [(rows,), (rows, 1)], dev)
-    _need(y, "y", torch.bfloat16, [(rows, inter)], dev)
-    _check(lib().swiglu_clamped_fwd(_ptr(x), _ptr(probs), _ptr(y), rows, inter, float(limit),
-                                    _stream_handle(x, stream)), "swiglu_clamped_fwd")
+    _need(y, "y", x.dtype, [(rows, inter)], dev)
+    st = _stream_handle(x, stream)
+    if code == 0:
+        status = lib().swiglu_clamped_fwd(_ptr(x), _ptr(probs), _ptr(y), rows, inter, float(limit), st)
+    else:
+        status = lib().swiglu_clamped_fwd_typed(_ptr(x), _ptr(probs), _ptr(y), rows, inter, float(limit), code, st)
+    _check(status, "swiglu_clamped_fwd")
 
 
 def swiglu_clamped_bwd(x, probs, grad_y, grad_x, grad_probs, limit: float, stream=None) -> None:
-    """grad_x[:, :inter] = d_gate, grad_x[:, inter:] = d_up, grad_probs[:] = per-row
-    probability gradient (skipped when grad_probs is None)."""
+    """grad_x[:, :inter] = d_gate, grad_x[:, inter:] = d_up (x's dtype), grad_probs[:] =
+    per-row probability gradient (fp32; skipped when grad_probs is None)."""
     rows, two_i = _rows_cols(x, "x")
     if two_i % 2:
         raise ValueError("x must have an even number of columns ([gate | up])")
-    inter, dev = two_i // 2, x.device
-    _need(x, "x", torch.bfloat16, [(rows, two_i)], dev)
+    inter, dev, code = two_i // 2, x.device, _code(x, "x")
+    _need(x, "x", x.dtype, [(rows, two_i)], dev)
     _need(probs, "probs", torch.float32, [(rows,), (rows, 1)], dev)
-    _need(grad_y, "grad_y", torch.bfloat16, [(rows, inter)], dev)
-    _need(grad_x, "grad_x", torch.bfloat16, [(rows, two_i)], dev)
+    _need(grad_y, "grad_y", x.dtype, [(rows, inter)], dev)
+    _need(grad_x, "grad_x", x.dtype, [(rows, two_i)], dev)
     if grad_probs is not None:
         _need(grad_probs, "grad_probs", torch.float32, [(rows,), (rows, 1)], dev)
-    _check(lib().swiglu_clamped_bwd(_ptr(x), _ptr(probs), _ptr(grad_y), _ptr(grad_x), _ptr(grad_probs),
-                                    rows, inter, float(limit), _stream_handle(x, stream)), "swiglu_clamped_bwd")
+    st = _stream_handle(x, stream)
+    if code == 0:
+        status = lib().swiglu_clamped_bwd(_ptr(x), _ptr(probs), _ptr(grad_y), _ptr(grad_x), _ptr(grad_probs), rows,
+                                          inter, float(limit), st)
+    else:
+        status = lib().swiglu_clamped_bwd_typed(_ptr(x), _ptr(probs), _ptr(grad_y), _ptr(grad_x), _ptr(grad_probs),
+                                                rows, inter, float(limit), code, st)
+    _check(status, "swiglu_clamped_bwd")
 
 
 def router_weight_mul_fwd(x, probs, out, stream=None) -> None:
-    """out[:] = bf16(fp32(x) * probs); x, out bf16 [rows, hidden]; probs fp32 [rows] or [rows, 1]."""
+    """out[:] = fp32(x) * probs rounded to out's dtype; x [rows, hidden] (bf16, fp16
+    or fp32), out of x's dtype or fp32; probs fp32 [rows] or [rows, 1]."""
     rows, hidden = _rows_cols(x, "x")
-    dev = x.device
-    _need(x, "x", torch.bfloat16, [(rows, hidden)], dev)
+    dev, xc = x.device, _code(x, "x")
+    _need(x, "x", x.dtype, [(rows, hidden)], dev)
     _need(probs, "probs", torch.float32, [(rows,), (rows, 1)], dev)
-    _need(out, "out", torch.bfloat16, [(rows, hidden)], dev)
-    _check(lib().router_weight_mul_fwd(_ptr(x), _ptr(probs), _ptr(out), rows, hidden,
-                                       _stream_handle(x, stream)), "router_weight_mul_fwd")
+    _need(out, "out", out.dtype, [(rows, hidden)], dev)
+    oc = _code(out, "out")
+    st = _stream_handle(x, stream)
+    if xc == 0 and oc == 0:
+        status = lib().router_weight_mul_fwd(_ptr(x), _ptr(probs), _ptr(out), rows, hidden, st)
+    else:
+        status = lib().router_weight_mul_fwd_typed(_ptr(x), xc, _ptr(probs), _ptr(out), oc, rows, hidden, st)
+    _check(status, "router_weight_mul_fwd")
 
 
 def router_weight_mul_bwd(grad_out, x, probs, grad_x, grad_probs, stream=None) -> None:
-    """grad_x[:] = bf16(fp32(grad_out) * probs); grad_probs[:] = sum_k grad_out * x (fp32).
+    """grad_x[:] = fp32(grad_out) * probs rounded to grad_x's dtype (x's dtype);
+    grad_probs[:] = sum_k grad_out * x (fp32). grad_out has the output's dtype.
     x and grad_probs may both be None (probabilities without gradient)."""
     rows, hidden = _rows_cols(grad_out, "grad_out")
     dev = grad_out.device
-    _need(grad_out, "grad_out", torch.bfloat16, [(rows, hidden)], dev)
+    _need(grad_out, "grad_out", grad_out.dtype, [(rows, hidden)], dev)
+    _need(grad_x, "grad_x", grad_x.dtype, [(rows, hidden)], dev)
+    xc, oc = _code(grad_x, "grad_x"), _code(grad_out, "grad_out")
     if grad_probs is not None:
-        _need(x, "x", torch.bfloat16, [(rows, hidden)], dev)
+        _need(x, "x", grad_x.dtype, [(rows, hidden)], dev)
         _need(grad_probs, "grad_probs", torch.float32, [(rows,), (rows, 1)], dev)
     _need(probs, "probs", torch.float32, [(rows,), (rows, 1)], dev)
-    _need(grad_x, "grad_x", torch.bfloat16, [(rows, hidden)], dev)
-    _check(lib().router_weight_mul_bwd(_ptr(grad_out), _ptr(x) if grad_probs is not None else None, _ptr(probs),
-                                       _ptr(grad_x), _ptr(grad_probs), rows, hidden,
-                                       _stream_handle(grad_out, stream)), "router_weight_mul_bwd")
+    xp = _ptr(x) if grad_probs is not None else None
+    st = _stream_handle(grad_out, stream)
+    if xc == 0 and oc == 0:
+        status = lib().router_weight_mul_bwd(_ptr(grad_out), xp, _ptr(probs), _ptr(grad_x), _ptr(grad_probs), rows,
+                                             hidden, st)
+    else:
+        status = lib().router_weight_mul_bwd_typed(_ptr(grad_out), oc, xp, xc, _ptr(probs), _ptr(grad_x),
+                                                   _ptr(grad_probs), rows, hidden, st)
+    _check(status, "router_weight_mul_bwd")
 
 
 # ---- allocating helpers and autograd wrappers ------------------------------
 
 def swiglu_clamped(x, probs, limit: float):
-    y = torch.empty((x.shape[0], x.shape[1] // 2), dtype=torch.bfloat16, device=x.device)
+    y = torch.empty((x.shape[0], x.shape[1] // 2), dtype=x.dtype, device=x.device)
     swiglu_clamped_fwd(x, probs, y, limit)
     return y
 
 
-def router_weight_mul(x, probs):
-    out = torch.empty_like(x)
+def router_weight_mul(x, probs, out_dtype=None):
+    out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     router_weight_mul_fwd(x, probs, out)
     return out
 
@@ -200,23 +242,25 @@ class SwigluClamped(torch.autograd.Function):
 
 
 class RouterWeightMul(torch.autograd.Function):
-    """bf16(fp32(x) * probs) with the HIP forward and a one-pass backward. x is saved
-    only when probs needs a gradient (it is read only for that gradient)."""
+    """fp32(x) * probs rounded to out_dtype (default: x's dtype; float32 for a
+    scatter-add combine) with the HIP forward and a one-pass backward. x is
+    saved only when probs needs a gradient (it is read only for that gradient)."""
 
     @staticmethod
-    def forward(ctx, x, probs):
+    def forward(ctx, x, probs, out_dtype=None):
         x = x.contiguous()
         probs = probs.contiguous()
         save_x = probs.requires_grad
         ctx.save_for_backward(x if save_x else None, probs)
         ctx.save_x = save_x
-        return router_weight_mul(x, probs)
+        ctx.x_dtype = x.dtype
+        return router_weight_mul(x, probs, out_dtype)
 
     @staticmethod
     def backward(ctx, grad_out):
         x, probs = ctx.saved_tensors
         grad_out = grad_out.contiguous()
-        grad_x = torch.empty_like(grad_out)
+        grad_x = torch.empty(grad_out.shape, dtype=ctx.x_dtype, device=grad_out.device)
         grad_probs = torch.empty_like(probs) if ctx.save_x else None
         router_weight_mul_bwd(grad_out, x, probs, grad_x, grad_probs)
-        return grad_x, grad_probs
+        return grad_x, grad_probs, None

@@ -47,5 +47,15 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
     return out
 
 
+def device_asm(source: str, out: str) -> str:
+    """gfx950 assembly of one source, built with the library's own flags."""
+    flags = [f for f in FLAGS if f not in ("-fPIC", "-shared")]
+    cmd = [HIPCC, *flags, "--cuda-device-only", "-S", f"-I{INCLUDE}", f"-I{CSRC}", source, "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc -S failed:\n" + res.stdout + res.stderr)
+    return out
+
+
 if __name__ == "__main__":
     build(verbose="-v" in sys.argv)

@@ -4,14 +4,15 @@
 // _RouterWeightMulFunction, _rw_fwd_core, _rw_bwd_x_core, _rw_bwd_probs_core):
 // on the expert down-projection output x [tokens, hidden] with one fp32
 // routing probability per row,
-//   out        = bf16(fp32(x) * p)                 (bitwise equal to the eager multiply)
-//   grad_x     = bf16(fp32(grad_out) * p)
+//   out        = round_out(fp32(x) * p)             (bitwise equal to the eager multiply)
+//   grad_x     = round_x(fp32(grad_out) * p)
 //   grad_probs = sum_k fp32(grad_out) * fp32(x)     (fp32)
-// The page computes the two gradients with two cores, i.e. two passes over
-// grad_out; here both come out of one pass (grad_out and x read once).
+// where the output (and so grad_out) is x's dtype or fp32. The page computes
+// the two gradients with two cores, i.e. two passes over grad_out; here both
+// come out of one pass (grad_out and x read once).
 //
 // Kernel shape: as for the SwiGLU kernels, a group of G lanes owns a row and
-// walks it in 16-byte nontemporal vectors (8 bf16), V vectors per lane in
+// walks it in nontemporal vectors of 8 elements, V vectors per lane in
 // flight, spread over several wavefronts per row (see the launchers); the row
 // sum is a register accumulator reduced with cross-lane shuffles and, across
 // wavefronts, a few LDS slots. The forward needs no reduction but uses the
@@ -27,81 +28,99 @@ constexpr int kBlock = 256;
 
 // G lanes own a row (G <= 64: part of a wavefront; G = 64*W: W wavefronts),
 // B threads per block. The row loop advances whole blocks so that every thread
-// of a block runs the same iterations (row_sum may hold a barrier).
-template <int G, int V, int B>
-__global__ __launch_bounds__(B) void router_weight_mul_fwd_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ probs, uint16_t* __restrict__ out, int64_t rows,
-    int64_t hidden) {
+// of a block runs the same iterations (row_sum may hold a barrier). TX is the
+// dtype of x and grad_x, TO that of out and grad_out.
+template <int TX, int TO, int G, int V, int B>
+__global__ __launch_bounds__(B) void router_weight_mul_fwd_kernel(const void* __restrict__ x,
+                                                                  const float* __restrict__ probs,
+                                                                  void* __restrict__ out, int64_t rows,
+                                                                  int64_t hidden) {
+    using EX = Elem<TX>;
+    using EO = Elem<TO>;
+    constexpr bool kSplit = TX == MOE_EPI_F32 || TO == MOE_EPI_F32;  // the vector map (epi_common.h)
     constexpr int kRows = B / G;
-    const int lane = threadIdx.x % G;
-    const int64_t nvec = hidden / 8;
+    const uint32_t lane = threadIdx.x % G;
+    const uint32_t nvec = static_cast<uint32_t>(hidden / 8);
     for (int64_t rb = static_cast<int64_t>(blockIdx.x) * kRows; rb < rows;
          rb += static_cast<int64_t>(gridDim.x) * kRows) {
-        const int64_t r = rb + threadIdx.x / G;
+        const int64_t r = rb + group_in_block<G>();
         if (r >= rows) continue;
-        const uint16_t* xr = x + r * hidden;
-        uint16_t* orow = out + r * hidden;
+        const void* xr = row_at<TX>(x, r * hidden);
+        void* outr = row_at<TO>(out, r * hidden);
         const float p = probs[r];
-        for (int64_t c0 = lane; c0 < nvec; c0 += static_cast<int64_t>(G) * V) {
-            u32x4 v[V];
+        for (uint32_t c0 = lane; c0 < nvec; c0 += G * V) {
+            typename EX::Raw v[V];
+            Quads q[V];
+#pragma unroll
+            for (int k = 0; k < V; ++k) q[k] = quads_of<G, kSplit>(c0 + k * G, lane, nvec);
 #pragma unroll
             for (int k = 0; k < V; ++k)
-                if (c0 + k * G < nvec) v[k] = load_stream(xr + (c0 + k * G) * 8);
+                if (c0 + k * G < nvec) v[k] = EX::template load<kSplit>(xr, q[k]);
 #pragma unroll
             for (int k = 0; k < V; ++k) {
                 if (c0 + k * G < nvec) {
-                    u32x4 o;
+                    float f[8];
+                    EX::unpack(v[k], f);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(bf16_lo(v[k][i]) * p, bf16_hi(v[k][i]) * p);
-                    store_stream(orow + (c0 + k * G) * 8, o);
+                    for (int e = 0; e < 8; ++e) f[e] = f[e] * p;
+                    EO::template store<kSplit>(outr, q[k], EO::pack(f));
                 }
             }
         }
     }
 }
 
-template <int G, int V, int B, bool kGradProbs>
-__global__ __launch_bounds__(B) void router_weight_mul_bwd_kernel(
-    const uint16_t* __restrict__ grad_out, const uint16_t* __restrict__ x, const float* __restrict__ probs,
-    uint16_t* __restrict__ grad_x, float* __restrict__ grad_probs, int64_t rows, int64_t hidden) {
+template <int TX, int TO, int G, int V, int B, bool kGradProbs>
+__global__ __launch_bounds__(B) __attribute__((amdgpu_waves_per_eu(waves_for_two_blocks(B)))) void
+router_weight_mul_bwd_kernel(const void* __restrict__ grad_out, const void* __restrict__ x,
+                             const float* __restrict__ probs, void* __restrict__ grad_x,
+                             float* __restrict__ grad_probs, int64_t rows, int64_t hidden) {
+    using EX = Elem<TX>;
+    using EO = Elem<TO>;
+    constexpr bool kSplit = TX == MOE_EPI_F32 || TO == MOE_EPI_F32;  // the vector map (epi_common.h)
     constexpr int kRows = B / G;
     __shared__ float part[B / 64 > 0 ? B / 64 : 1];
-    const int lane = threadIdx.x % G;
-    const int64_t nvec = hidden / 8;
+    const uint32_t lane = threadIdx.x % G;
+    const uint32_t nvec = static_cast<uint32_t>(hidden / 8);
     for (int64_t rb = static_cast<int64_t>(blockIdx.x) * kRows; rb < rows;
          rb += static_cast<int64_t>(gridDim.x) * kRows) {
-        const int64_t r = rb + threadIdx.x / G;
+        const int64_t r = rb + group_in_block<G>();
         float acc = 0.0f;
         if (r < rows) {
-            const uint16_t* gr = grad_out + r * hidden;
-            const uint16_t* xr = x + r * hidden;
-            uint16_t* gxr = grad_x + r * hidden;
+            const void* gor = row_at<TO>(grad_out, r * hidden);
+            const void* xr = kGradProbs ? row_at<TX>(x, r * hidden) : nullptr;
+            void* gxr = row_at<TX>(grad_x, r * hidden);
             const float p = probs[r];
-            for (int64_t c0 = lane; c0 < nvec; c0 += static_cast<int64_t>(G) * V) {
-                u32x4 g[V], xv[V];
+            for (uint32_t c0 = lane; c0 < nvec; c0 += G * V) {
+                typename EO::Raw g[V];
+                typename EX::Raw xv[V];
+                Quads q[V];
+#pragma unroll
+                for (int k = 0; k < V; ++k) q[k] = quads_of<G, kSplit>(c0 + k * G, lane, nvec);
 #pragma unroll
                 for (int k = 0; k < V; ++k)
-                    if (c0 + k * G < nvec) g[k] = load_stream(gr + (c0 + k * G) * 8);
+                    if (c0 + k * G < nvec) g[k] = EO::template load<kSplit>(gor, q[k]);
                 if (kGradProbs) {
 #pragma unroll
                     for (int k = 0; k < V; ++k)
-                        if (c0 + k * G < nvec) xv[k] = load_stream(xr + (c0 + k * G) * 8);
+                        if (c0 + k * G < nvec) xv[k] = EX::template load<kSplit>(xr, q[k]);
                 }
 #pragma unroll
                 for (int k = 0; k < V; ++k) {
                     if (c0 + k * G < nvec) {
-                        u32x4 o;
+                        float gf[8], o[8];
+                        EO::unpack(g[k], gf);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float g0 = bf16_lo(g[k][i]), g1 = bf16_hi(g[k][i]);
-                            o[i] = pack_bf16x2(g0 * p, g1 * p);
-                            // a product of two bf16 values is exact in fp32
-                            if (kGradProbs) {
-                                acc = __fmaf_rn(g0, bf16_lo(xv[k][i]), acc);
-                                acc = __fmaf_rn(g1, bf16_hi(xv[k][i]), acc);
-                            }
+                        for (int e = 0; e < 8; ++e) o[e] = gf[e] * p;
+                        if (kGradProbs) {
+                            float xf[8];
+                            EX::unpack(xv[k], xf);
+                            // bf16 x bf16 products are exact in fp32; for wider
+                            // types the fused multiply-add rounds once
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) acc = __fmaf_rn(gf[e], xf[e], acc);
                         }
-                        store_stream(gxr + (c0 + k * G) * 8, o);
+                        EX::template store<kSplit>(gxr, q[k], EX::pack(o));
                     }
                 }
             }
@@ -113,23 +132,26 @@ __global__ __launch_bounds__(B) void router_weight_mul_bwd_kernel(
     }
 }
 
-// per-element kernels (any hidden, 2-byte aligned tensors)
-__global__ __launch_bounds__(kBlock) void router_weight_mul_fwd_scalar_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ probs, uint16_t* __restrict__ out, int64_t rows,
-    int64_t hidden) {
+// per-element kernels (any hidden, element-aligned tensors)
+template <int TX, int TO>
+__global__ __launch_bounds__(kBlock) void router_weight_mul_fwd_scalar_kernel(const void* __restrict__ x,
+                                                                             const float* __restrict__ probs,
+                                                                             void* __restrict__ out, int64_t rows,
+                                                                             int64_t hidden) {
     constexpr int kRows = kBlock / 64;
     const int lane = threadIdx.x % 64;
     for (int64_t r = static_cast<int64_t>(blockIdx.x) * kRows + threadIdx.x / 64; r < rows;
          r += static_cast<int64_t>(gridDim.x) * kRows) {
         const float p = probs[r];
-        for (int64_t k = lane; k < hidden; k += 64) out[r * hidden + k] = to_bf16(bf16_at(x + r * hidden + k) * p);
+        for (int64_t k = lane; k < hidden; k += 64)
+            Elem<TO>::store1(out, r * hidden + k, Elem<TX>::load1(x, r * hidden + k) * p);
     }
 }
 
-template <bool kGradProbs>
+template <int TX, int TO, bool kGradProbs>
 __global__ __launch_bounds__(kBlock) void router_weight_mul_bwd_scalar_kernel(
-    const uint16_t* __restrict__ grad_out, const uint16_t* __restrict__ x, const float* __restrict__ probs,
-    uint16_t* __restrict__ grad_x, float* __restrict__ grad_probs, int64_t rows, int64_t hidden) {
+    const void* __restrict__ grad_out, const void* __restrict__ x, const float* __restrict__ probs,
+    void* __restrict__ grad_x, float* __restrict__ grad_probs, int64_t rows, int64_t hidden) {
     constexpr int kRows = kBlock / 64;
     const int lane = threadIdx.x % 64;
     for (int64_t r = static_cast<int64_t>(blockIdx.x) * kRows + threadIdx.x / 64; r < rows;
@@ -137,9 +159,9 @@ __global__ __launch_bounds__(kBlock) void router_weight_mul_bwd_scalar_kernel(
         const float p = probs[r];
         float acc = 0.0f;
         for (int64_t k = lane; k < hidden; k += 64) {
-            const float g = bf16_at(grad_out + r * hidden + k);
-            grad_x[r * hidden + k] = to_bf16(g * p);
-            if (kGradProbs) acc = __fmaf_rn(g, bf16_at(x + r * hidden + k), acc);
+            const float g = Elem<TO>::load1(grad_out, r * hidden + k);
+            Elem<TX>::store1(grad_x, r * hidden + k, g * p);
+            if (kGradProbs) acc = __fmaf_rn(g, Elem<TX>::load1(x, r * hidden + k), acc);
         }
         if (kGradProbs) {
             acc = group_sum<64>(acc);
@@ -148,7 +170,7 @@ __global__ __launch_bounds__(kBlock) void router_weight_mul_bwd_scalar_kernel(
     }
 }
 
-// Shapes (measured on MI355X at 65536 x 7168; nontemporal 16-byte accesses):
+// Shapes (measured on MI355X at 65536 x 7168 bf16; nontemporal accesses):
 //   forward:  2 wavefronts per row, 256-thread blocks, up to 16 vectors per
 //             lane per pass (7168: 7 per lane, the whole row in one pass);
 //   backward: 2 vectors per lane and as many wavefronts per row as that needs
@@ -156,85 +178,179 @@ __global__ __launch_bounds__(kBlock) void router_weight_mul_bwd_scalar_kernel(
 //             threads. Against one wavefront per row (14 vectors per lane) the
 //             forward ran 2% and the backward 8% faster: a row's loads are
 //             issued from several SIMDs at once.
-template <int G, int V, int B>
-void launch_fwd(const uint16_t* x, const float* probs, uint16_t* out, int64_t rows, int64_t hidden, hipStream_t st) {
-    hipLaunchKernelGGL((router_weight_mul_fwd_kernel<G, V, B>), dim3(grid_for_rows(rows, B / G)), dim3(B), 0, st, x,
-                       probs, out, rows, hidden);
+//   The same shapes serve every dtype (they count elements).
+template <int TX, int TO, int G, int V, int B>
+void launch_fwd(const void* x, const float* probs, void* out, int64_t rows, int64_t hidden, hipStream_t st) {
+    hipLaunchKernelGGL((router_weight_mul_fwd_kernel<TX, TO, G, V, B>), dim3(grid_for_rows(rows, B / G)), dim3(B), 0,
+                       st, x, probs, out, rows, hidden);
 }
 
-template <int G, int V, int B>
-void launch_bwd(const uint16_t* go, const uint16_t* x, const float* probs, uint16_t* gx, float* gp, int64_t rows,
-                int64_t hidden, hipStream_t st) {
+template <int TX, int TO, int G, int V, int B>
+void launch_bwd(const void* go, const void* x, const float* probs, void* gx, float* gp, int64_t rows, int64_t hidden,
+                hipStream_t st) {
     const dim3 grid(grid_for_rows(rows, B / G));
     if (gp)
-        hipLaunchKernelGGL((router_weight_mul_bwd_kernel<G, V, B, true>), grid, dim3(B), 0, st, go, x, probs, gx, gp,
-                           rows, hidden);
+        hipLaunchKernelGGL((router_weight_mul_bwd_kernel<TX, TO, G, V, B, true>), grid, dim3(B), 0, st, go, x, probs,
+                           gx, gp, rows, hidden);
     else
-        hipLaunchKernelGGL((router_weight_mul_bwd_kernel<G, V, B, false>), grid, dim3(B), 0, st, go, x, probs, gx, gp,
-                           rows, hidden);
+        hipLaunchKernelGGL((router_weight_mul_bwd_kernel<TX, TO, G, V, B, false>), grid, dim3(B), 0, st, go, x, probs,
+                           gx, gp, rows, hidden);
 }
 
-void dispatch_fwd(const uint16_t* x, const float* probs, uint16_t* out, int64_t rows, int64_t hidden,
-                  hipStream_t st) {
+template <int TX, int TO>
+void dispatch_fwd(const void* x, const float* probs, void* out, int64_t rows, int64_t hidden, hipStream_t st) {
     const int64_t nvec = hidden / 8;
     if (nvec < 64) {
         switch (small_group(nvec)) {
-            case 8: return launch_fwd<8, 1, 256>(x, probs, out, rows, hidden, st);
-            case 16: return launch_fwd<16, 1, 256>(x, probs, out, rows, hidden, st);
-            default: return launch_fwd<32, 1, 256>(x, probs, out, rows, hidden, st);
+            case 8: return launch_fwd<TX, TO, 8, 1, 256>(x, probs, out, rows, hidden, st);
+            case 16: return launch_fwd<TX, TO, 16, 1, 256>(x, probs, out, rows, hidden, st);
+            default: return launch_fwd<TX, TO, 32, 1, 256>(x, probs, out, rows, hidden, st);
         }
     }
-    if (nvec < 128) return launch_fwd<64, 2, 256>(x, probs, out, rows, hidden, st);
+    if (nvec < 128) return launch_fwd<TX, TO, 64, 2, 256>(x, probs, out, rows, hidden, st);
     switch (ceil_div(nvec, 128)) {  // vectors per lane with 128 lanes per row
-        case 1: return launch_fwd<128, 1, 256>(x, probs, out, rows, hidden, st);
-        case 2: return launch_fwd<128, 2, 256>(x, probs, out, rows, hidden, st);
-        case 3: return launch_fwd<128, 3, 256>(x, probs, out, rows, hidden, st);
-        case 4: return launch_fwd<128, 4, 256>(x, probs, out, rows, hidden, st);
-        case 5: return launch_fwd<128, 5, 256>(x, probs, out, rows, hidden, st);
-        case 6: return launch_fwd<128, 6, 256>(x, probs, out, rows, hidden, st);
-        case 7: return launch_fwd<128, 7, 256>(x, probs, out, rows, hidden, st);
-        case 8: return launch_fwd<128, 8, 256>(x, probs, out, rows, hidden, st);
-        case 9: case 10: return launch_fwd<128, 10, 256>(x, probs, out, rows, hidden, st);
-        case 11: case 12: return launch_fwd<128, 12, 256>(x, probs, out, rows, hidden, st);
-        case 13: case 14: return launch_fwd<128, 14, 256>(x, probs, out, rows, hidden, st);
-        default: return launch_fwd<128, 16, 256>(x, probs, out, rows, hidden, st);
+        case 1: return launch_fwd<TX, TO, 128, 1, 256>(x, probs, out, rows, hidden, st);
+        case 2: return launch_fwd<TX, TO, 128, 2, 256>(x, probs, out, rows, hidden, st);
+        case 3: return launch_fwd<TX, TO, 128, 3, 256>(x, probs, out, rows, hidden, st);
+        case 4: return launch_fwd<TX, TO, 128, 4, 256>(x, probs, out, rows, hidden, st);
+        case 5: case 6: return launch_fwd<TX, TO, 128, 6, 256>(x, probs, out, rows, hidden, st);
+        case 7: return launch_fwd<TX, TO, 128, 7, 256>(x, probs, out, rows, hidden, st);
+        case 8: return launch_fwd<TX, TO, 128, 8, 256>(x, probs, out, rows, hidden, st);
+        case 9: case 10: case 11: case 12: return launch_fwd<TX, TO, 128, 12, 256>(x, probs, out, rows, hidden, st);
+        default: return launch_fwd<TX, TO, 128, 16, 256>(x, probs, out, rows, hidden, st);  // wider rows: passes
     }
 }
 
-void dispatch_bwd(const uint16_t* go, const uint16_t* x, const float* probs, uint16_t* gx, float* gp, int64_t rows,
+template <int TX, int TO>
+void dispatch_bwd(const void* go, const void* x, const float* probs, void* gx, float* gp, int64_t rows,
                   int64_t hidden, hipStream_t st) {
     const int64_t nvec = hidden / 8;
     if (nvec < 64) {
         switch (small_group(nvec)) {
-            case 8: return launch_bwd<8, 1, 256>(go, x, probs, gx, gp, rows, hidden, st);
-            case 16: return launch_bwd<16, 1, 256>(go, x, probs, gx, gp, rows, hidden, st);
-            default: return launch_bwd<32, 1, 256>(go, x, probs, gx, gp, rows, hidden, st);
+            case 8: return launch_bwd<TX, TO, 8, 1, 256>(go, x, probs, gx, gp, rows, hidden, st);
+            case 16: return launch_bwd<TX, TO, 16, 1, 256>(go, x, probs, gx, gp, rows, hidden, st);
+            default: return launch_bwd<TX, TO, 32, 1, 256>(go, x, probs, gx, gp, rows, hidden, st);
         }
     }
     switch (ceil_div(nvec, 128)) {  // wavefronts per row with 2 vectors per lane
-        case 1: return launch_bwd<64, 2, 128>(go, x, probs, gx, gp, rows, hidden, st);
-        case 2: return launch_bwd<128, 2, 256>(go, x, probs, gx, gp, rows, hidden, st);
-        case 3: return launch_bwd<192, 2, 384>(go, x, probs, gx, gp, rows, hidden, st);
-        case 4: return launch_bwd<256, 2, 512>(go, x, probs, gx, gp, rows, hidden, st);
-        case 5: return launch_bwd<320, 2, 640>(go, x, probs, gx, gp, rows, hidden, st);
-        case 6: return launch_bwd<384, 2, 768>(go, x, probs, gx, gp, rows, hidden, st);
-        case 7: return launch_bwd<448, 2, 896>(go, x, probs, gx, gp, rows, hidden, st);
-        case 8: return launch_bwd<512, 2, 1024>(go, x, probs, gx, gp, rows, hidden, st);
-        case 9: return launch_bwd<576, 2, 576>(go, x, probs, gx, gp, rows, hidden, st);
-        case 10: return launch_bwd<640, 2, 640>(go, x, probs, gx, gp, rows, hidden, st);
-        case 11: return launch_bwd<704, 2, 704>(go, x, probs, gx, gp, rows, hidden, st);
-        case 12: return launch_bwd<768, 2, 768>(go, x, probs, gx, gp, rows, hidden, st);
-        case 13: return launch_bwd<832, 2, 832>(go, x, probs, gx, gp, rows, hidden, st);
-        case 14: return launch_bwd<896, 2, 896>(go, x, probs, gx, gp, rows, hidden, st);
-        case 15: return launch_bwd<960, 2, 960>(go, x, probs, gx, gp, rows, hidden, st);
-        default: return launch_bwd<1024, 2, 1024>(go, x, probs, gx, gp, rows, hidden, st);  // wider rows: passes
+        case 1: return launch_bwd<TX, TO, 64, 2, 128>(go, x, probs, gx, gp, rows, hidden, st);
+        case 2: return launch_bwd<TX, TO, 128, 2, 256>(go, x, probs, gx, gp, rows, hidden, st);
+        case 3: return launch_bwd<TX, TO, 192, 2, 384>(go, x, probs, gx, gp, rows, hidden, st);
+        case 4: return launch_bwd<TX, TO, 256, 2, 512>(go, x, probs, gx, gp, rows, hidden, st);
+        case 5: return launch_bwd<TX, TO, 320, 2, 640>(go, x, probs, gx, gp, rows, hidden, st);
+        case 6: return launch_bwd<TX, TO, 384, 2, 768>(go, x, probs, gx, gp, rows, hidden, st);
+        case 7: return launch_bwd<TX, TO, 448, 2, 896>(go, x, probs, gx, gp, rows, hidden, st);
+        case 8: return launch_bwd<TX, TO, 512, 2, 1024>(go, x, probs, gx, gp, rows, hidden, st);
+        case 9: case 10: case 11: case 12: return launch_bwd<TX, TO, 768, 2, 768>(go, x, probs, gx, gp, rows, hidden, st);
+        default: return launch_bwd<TX, TO, 1024, 2, 1024>(go, x, probs, gx, gp, rows, hidden, st);  // wider: passes
     }
 }
 
-int check_router(int64_t rows, int64_t hidden, int64_t* h_bytes, int64_t* p_bytes) {
+// The (x, output) dtype pairs: the output is x's dtype or float32.
+enum class Pair { kBB, kBF, kHH, kHF, kFF, kBad };
+
+Pair pair_of(int x_dtype, int out_dtype) {
+    if (x_dtype == MOE_EPI_BF16 && out_dtype == MOE_EPI_BF16) return Pair::kBB;
+    if (x_dtype == MOE_EPI_BF16 && out_dtype == MOE_EPI_F32) return Pair::kBF;
+    if (x_dtype == MOE_EPI_F16 && out_dtype == MOE_EPI_F16) return Pair::kHH;
+    if (x_dtype == MOE_EPI_F16 && out_dtype == MOE_EPI_F32) return Pair::kHF;
+    if (x_dtype == MOE_EPI_F32 && out_dtype == MOE_EPI_F32) return Pair::kFF;
+    return Pair::kBad;
+}
+
+template <int TX, int TO>
+void run_fwd(const void* x, const float* probs, void* out, int64_t rows, int64_t hidden, bool vec, hipStream_t st) {
+    if (vec)
+        dispatch_fwd<TX, TO>(x, probs, out, rows, hidden, st);
+    else
+        hipLaunchKernelGGL((router_weight_mul_fwd_scalar_kernel<TX, TO>), dim3(grid_for_rows(rows, kBlock / 64)),
+                           dim3(kBlock), 0, st, x, probs, out, rows, hidden);
+}
+
+template <int TX, int TO>
+void run_bwd(const void* go, const void* x, const float* probs, void* gx, float* gp, int64_t rows, int64_t hidden,
+             bool vec, hipStream_t st) {
+    if (vec) {
+        dispatch_bwd<TX, TO>(go, x, probs, gx, gp, rows, hidden, st);
+        return;
+    }
+    const dim3 grid(grid_for_rows(rows, kBlock / 64));
+    if (gp)
+        hipLaunchKernelGGL((router_weight_mul_bwd_scalar_kernel<TX, TO, true>), grid, dim3(kBlock), 0, st, go, x,
+                           probs, gx, gp, rows, hidden);
+    else
+        hipLaunchKernelGGL((router_weight_mul_bwd_scalar_kernel<TX, TO, false>), grid, dim3(kBlock), 0, st, go, x,
+                           probs, gx, gp, rows, hidden);
+}
+
+int check_router(int64_t rows, int64_t hidden, int x_dtype, int out_dtype, int64_t* x_bytes, int64_t* o_bytes,
+                 int64_t* p_bytes) {
+    if (!dtype_ok(x_dtype) || !dtype_ok(out_dtype) || pair_of(x_dtype, out_dtype) == Pair::kBad)
+        return MOE_EPI_ERR_BAD_DTYPE;
     if (rows < 0 || hidden <= 0) return MOE_EPI_ERR_BAD_SHAPE;
-    if (!bytes_ok(rows, hidden, 2, h_bytes) || !bytes_ok(rows, 1, 4, p_bytes)) return MOE_EPI_ERR_BAD_SHAPE;
+    if (!bytes_ok(rows, hidden, elem_bytes(x_dtype), x_bytes) || !bytes_ok(rows, hidden, elem_bytes(out_dtype), o_bytes) ||
+        !bytes_ok(rows, 1, 4, p_bytes))
+        return MOE_EPI_ERR_BAD_SHAPE;
     return MOE_EPI_SUCCESS;
+}
+
+int router_fwd_impl(const void* x, int x_dtype, const float* probs, void* out, int out_dtype, int64_t rows,
+                    int64_t hidden, void* stream) {
+    int64_t xb, ob, pb;
+    int st = check_router(rows, hidden, x_dtype, out_dtype, &xb, &ob, &pb);
+    if (st != MOE_EPI_SUCCESS) return st;
+    if (rows == 0) return MOE_EPI_SUCCESS;
+    if (!x || !probs || !out) return MOE_EPI_ERR_NULL_POINTER;
+    if (!aligned(x, elem_bytes(x_dtype)) || !aligned(out, elem_bytes(out_dtype)) || !aligned(probs, 4))
+        return MOE_EPI_ERR_MISALIGNED;
+    const Range rx = range_of(x, xb), rp = range_of(probs, pb), ro = range_of(out, ob);
+    if (overlaps(ro, rx) || overlaps(ro, rp)) return MOE_EPI_ERR_ALIAS;
+
+    hipStream_t s = as_stream(stream);
+    (void)hipGetLastError();
+    const int wide = elem_bytes(x_dtype) > elem_bytes(out_dtype) ? elem_bytes(x_dtype) : elem_bytes(out_dtype);
+    const bool vec = hidden % 8 == 0 && row_fits_u32_offsets(hidden, wide) && aligned(x, 16) && aligned(out, 16);
+    switch (pair_of(x_dtype, out_dtype)) {
+        case Pair::kBB: run_fwd<MOE_EPI_BF16, MOE_EPI_BF16>(x, probs, out, rows, hidden, vec, s); break;
+        case Pair::kBF: run_fwd<MOE_EPI_BF16, MOE_EPI_F32>(x, probs, out, rows, hidden, vec, s); break;
+        case Pair::kHH: run_fwd<MOE_EPI_F16, MOE_EPI_F16>(x, probs, out, rows, hidden, vec, s); break;
+        case Pair::kHF: run_fwd<MOE_EPI_F16, MOE_EPI_F32>(x, probs, out, rows, hidden, vec, s); break;
+        default: run_fwd<MOE_EPI_F32, MOE_EPI_F32>(x, probs, out, rows, hidden, vec, s); break;
+    }
+    return launch_status();
+}
+
+int router_bwd_impl(const void* grad_out, int go_dtype, const void* x, int x_dtype, const float* probs, void* grad_x,
+                    float* grad_probs, int64_t rows, int64_t hidden, void* stream) {
+    int64_t xb, ob, pb;
+    int st = check_router(rows, hidden, x_dtype, go_dtype, &xb, &ob, &pb);
+    if (st != MOE_EPI_SUCCESS) return st;
+    if (rows == 0) return MOE_EPI_SUCCESS;
+    if (!grad_out || !probs || !grad_x || (grad_probs && !x)) return MOE_EPI_ERR_NULL_POINTER;
+    if (!grad_probs) x = nullptr;  // x is only read for the probability gradient
+    const int xe = elem_bytes(x_dtype);
+    if (!aligned(grad_out, elem_bytes(go_dtype)) || !aligned(grad_x, xe) || !aligned(probs, 4) ||
+        (x && !aligned(x, xe)) || (grad_probs && !aligned(grad_probs, 4)))
+        return MOE_EPI_ERR_MISALIGNED;
+    const Range rgo = range_of(grad_out, ob), rx = range_of(x, x ? xb : 0), rp = range_of(probs, pb);
+    const Range rgx = range_of(grad_x, xb), rgp = range_of(grad_probs, grad_probs ? pb : 0);
+    if (overlaps(rgx, rgo) || overlaps(rgx, rx) || overlaps(rgx, rp) || overlaps(rgp, rgo) || overlaps(rgp, rx) ||
+        overlaps(rgp, rp) || overlaps(rgp, rgx))
+        return MOE_EPI_ERR_ALIAS;
+
+    hipStream_t s = as_stream(stream);
+    (void)hipGetLastError();
+    const int wide = xe > elem_bytes(go_dtype) ? xe : elem_bytes(go_dtype);
+    const bool vec = hidden % 8 == 0 && row_fits_u32_offsets(hidden, wide) && aligned(grad_out, 16) &&
+                     aligned(grad_x, 16) && (!x || aligned(x, 16));
+    switch (pair_of(x_dtype, go_dtype)) {
+        case Pair::kBB: run_bwd<MOE_EPI_BF16, MOE_EPI_BF16>(grad_out, x, probs, grad_x, grad_probs, rows, hidden, vec, s); break;
+        case Pair::kBF: run_bwd<MOE_EPI_BF16, MOE_EPI_F32>(grad_out, x, probs, grad_x, grad_probs, rows, hidden, vec, s); break;
+        case Pair::kHH: run_bwd<MOE_EPI_F16, MOE_EPI_F16>(grad_out, x, probs, grad_x, grad_probs, rows, hidden, vec, s); break;
+        case Pair::kHF: run_bwd<MOE_EPI_F16, MOE_EPI_F32>(grad_out, x, probs, grad_x, grad_probs, rows, hidden, vec, s); break;
+        default: run_bwd<MOE_EPI_F32, MOE_EPI_F32>(grad_out, x, probs, grad_x, grad_probs, rows, hidden, vec, s); break;
+    }
+    return launch_status();
 }
 
 }  // namespace
@@ -242,60 +358,26 @@ int check_router(int64_t rows, int64_t hidden, int64_t* h_bytes, int64_t* p_byte
 
 extern "C" int router_weight_mul_fwd(const uint16_t* x, const float* probs, uint16_t* out, int64_t rows,
                                      int64_t hidden, void* stream) {
-    using namespace moe_epi;
-    int64_t hb, pb;
-    int st = check_router(rows, hidden, &hb, &pb);
-    if (st != MOE_EPI_SUCCESS) return st;
-    if (rows == 0) return MOE_EPI_SUCCESS;
-    if (!x || !probs || !out) return MOE_EPI_ERR_NULL_POINTER;
-    if (!aligned(x, 2) || !aligned(out, 2) || !aligned(probs, 4)) return MOE_EPI_ERR_MISALIGNED;
-    const Range rx = range_of(x, hb), rp = range_of(probs, pb), ro = range_of(out, hb);
-    if (overlaps(ro, rx) || overlaps(ro, rp)) return MOE_EPI_ERR_ALIAS;
-
-    hipStream_t s = as_stream(stream);
-    (void)hipGetLastError();
-    if (hidden % 8 == 0 && aligned(x, 16) && aligned(out, 16)) {
-        dispatch_fwd(x, probs, out, rows, hidden, s);
-    } else {
-        hipLaunchKernelGGL(router_weight_mul_fwd_scalar_kernel, dim3(grid_for_rows(rows, kBlock / 64)), dim3(kBlock),
-                           0, s, x, probs, out, rows, hidden);
-    }
-    return launch_status();
+    return moe_epi::router_fwd_impl(x, MOE_EPI_BF16, probs, out, MOE_EPI_BF16, rows, hidden, stream);
 }
 
 extern "C" int router_weight_mul_bwd(const uint16_t* grad_out, const uint16_t* x, const float* probs,
                                      uint16_t* grad_x, float* grad_probs, int64_t rows, int64_t hidden,
                                      void* stream) {
-    using namespace moe_epi;
-    int64_t hb, pb;
-    int st = check_router(rows, hidden, &hb, &pb);
-    if (st != MOE_EPI_SUCCESS) return st;
-    if (rows == 0) return MOE_EPI_SUCCESS;
-    if (!grad_out || !probs || !grad_x || (grad_probs && !x)) return MOE_EPI_ERR_NULL_POINTER;
-    if (!grad_probs) x = nullptr;  // x is only read for the probability gradient
-    if (!aligned(grad_out, 2) || !aligned(grad_x, 2) || !aligned(probs, 4) || (x && !aligned(x, 2)) ||
-        (grad_probs && !aligned(grad_probs, 4)))
-        return MOE_EPI_ERR_MISALIGNED;
-    const Range rgo = range_of(grad_out, hb), rx = range_of(x, x ? hb : 0), rp = range_of(probs, pb);
-    const Range rgx = range_of(grad_x, hb), rgp = range_of(grad_probs, grad_probs ? pb : 0);
-    if (overlaps(rgx, rgo) || overlaps(rgx, rx) || overlaps(rgx, rp) || overlaps(rgp, rgo) || overlaps(rgp, rx) ||
-        overlaps(rgp, rp) || overlaps(rgp, rgx))
-        return MOE_EPI_ERR_ALIAS;
+    return moe_epi::router_bwd_impl(grad_out, MOE_EPI_BF16, x, MOE_EPI_BF16, probs, grad_x, grad_probs, rows, hidden,
+                                    stream);
+}
 
-    hipStream_t s = as_stream(stream);
-    (void)hipGetLastError();
-    if (hidden % 8 == 0 && aligned(grad_out, 16) && aligned(grad_x, 16) && (!x || aligned(x, 16))) {
-        dispatch_bwd(grad_out, x, probs, grad_x, grad_probs, rows, hidden, s);
-    } else {
-        const dim3 grid(grid_for_rows(rows, kBlock / 64));
-        if (grad_probs)
-            hipLaunchKernelGGL(router_weight_mul_bwd_scalar_kernel<true>, grid, dim3(kBlock), 0, s, grad_out, x,
-                               probs, grad_x, grad_probs, rows, hidden);
-        else
-            hipLaunchKernelGGL(router_weight_mul_bwd_scalar_kernel<false>, grid, dim3(kBlock), 0, s, grad_out, x,
-                               probs, grad_x, grad_probs, rows, hidden);
-    }
-    return launch_status();
+extern "C" int router_weight_mul_fwd_typed(const void* x, int x_dtype, const float* probs, void* out, int out_dtype,
+                                           int64_t rows, int64_t hidden, void* stream) {
+    return moe_epi::router_fwd_impl(x, x_dtype, probs, out, out_dtype, rows, hidden, stream);
+}
+
+extern "C" int router_weight_mul_bwd_typed(const void* grad_out, int grad_out_dtype, const void* x, int x_dtype,
+                                           const float* probs, void* grad_x, float* grad_probs, int64_t rows,
+                                           int64_t hidden, void* stream) {
+    return moe_epi::router_bwd_impl(grad_out, grad_out_dtype, x, x_dtype, probs, grad_x, grad_probs, rows, hidden,
+                                    stream);
 }
 
 extern "C" const char* moe_epi_status_string(int status) {
@@ -307,6 +389,7 @@ extern "C" const char* moe_epi_status_string(int status) {
         case MOE_EPI_ERR_ALIAS: return "an output overlaps an input or another output";
         case MOE_EPI_ERR_MISALIGNED: return "a pointer is not aligned to its element size";
         case MOE_EPI_ERR_LAUNCH: return "the HIP runtime reported a kernel launch error";
+        case MOE_EPI_ERR_BAD_DTYPE: return "unsupported dtype (or dtype pair)";
         default: return "unknown status";
     }
 }

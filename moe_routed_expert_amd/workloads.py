@@ -29,7 +29,9 @@ Readings taken where the workload text is loose:
   - top-8 renormalisation divides each group of 8 consecutive rows by the
     group's sum, computed in float64 and rounded once to float32;
   - normals are drawn in float32, scaled by sigma in float32 and rounded to
-    bfloat16 to nearest-even.
+    the storage dtype (bfloat16 or float16) to nearest-even; float32 storage
+    keeps the draws as they are (so a float32 workload holds the same draws
+    as its bfloat16 twin before rounding).
 Draws are made in fixed chunks of 4096 rows; each chunk and each kind of draw
 has its own PCG64 stream from numpy.random.SeedSequence(seed, spawn_key=(kind,
 chunk)), so a workload is the same on every machine and for any thread count.
@@ -52,6 +54,25 @@ def _to_bf16_bits(a: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
+# Storage dtypes: bfloat16 travels as uint16 bit patterns, float16 and float32
+# as numpy's own types.
+DTYPES = ("bf16", "f16", "f32")
+ELEM_BYTES = {"bf16": 2, "f16": 2, "f32": 4}
+
+
+def _to_storage(a: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 draws -> the storage dtype (rounded to nearest-even by torch/numpy)."""
+    if dtype == "bf16":
+        return _to_bf16_bits(a)
+    if dtype == "f16":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.float16).numpy()
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def storage_numpy_dtype(dtype: str):
+    return {"bf16": np.uint16, "f16": np.float16, "f32": np.float32}[dtype]
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str
@@ -71,24 +92,29 @@ class Workload:
     def x_cols(self) -> int:
         return 2 * self.cols if self.op == "swiglu" else self.cols
 
-    def fwd_bytes(self) -> int:
+    def fwd_bytes(self, dtype: str = "bf16", out_dtype: str | None = None) -> int:
         """Algorithmic HBM bytes of one forward pass (every input read once,
-        every output written once)."""
+        every output written once); out_dtype is the router output's dtype."""
+        e = ELEM_BYTES[dtype]
         if self.op == "swiglu":
-            return self.rows * (6 * self.cols + 4)
-        return self.rows * (4 * self.cols + 4)
+            return self.rows * (3 * e * self.cols + 4)
+        return self.rows * ((e + ELEM_BYTES[out_dtype or dtype]) * self.cols + 4)
 
-    def bwd_bytes(self, with_grad_probs: bool = True) -> int:
+    def bwd_bytes(self, with_grad_probs: bool = True, dtype: str = "bf16", out_dtype: str | None = None) -> int:
         """Algorithmic HBM bytes of one backward pass."""
+        e = ELEM_BYTES[dtype]
         if self.op == "swiglu":
-            return self.rows * (10 * self.cols + 4 + (4 if with_grad_probs else 0))
+            return self.rows * (5 * e * self.cols + 4 + (4 if with_grad_probs else 0))
+        eo = ELEM_BYTES[out_dtype or dtype]
         if with_grad_probs:
-            return self.rows * (6 * self.cols + 8)
-        return self.rows * (4 * self.cols + 4)
+            return self.rows * ((eo + 2 * e) * self.cols + 8)
+        return self.rows * ((eo + e) * self.cols + 4)
 
-    def generate(self, rows: int | None = None, threads: int | None = None) -> dict:
-        """Inputs as numpy arrays: x (uint16 bf16 bits [rows, x_cols]),
-        probs (float32 [rows]), grad_out (uint16 bf16 bits [rows, cols]).
+    def generate(self, rows: int | None = None, threads: int | None = None, dtype: str = "bf16",
+                 grad_dtype: str | None = None) -> dict:
+        """Inputs as numpy arrays: x ([rows, x_cols] of `dtype`), probs
+        (float32 [rows]), grad_out ([rows, cols] of `grad_dtype`, default
+        `dtype`). bf16 arrays are uint16 bit patterns.
 
         Each chunk of CHUNK_ROWS rows draws from its own streams, derived from
         (seed, stream kind, chunk index), so chunks can be drawn in parallel and
@@ -97,8 +123,9 @@ class Workload:
         if n < 0 or n > self.rows:
             raise ValueError("rows out of range")
         xc, gc = self.x_cols, self.cols
-        x = np.empty((n, xc), dtype=np.uint16)
-        gy = np.empty((n, gc), dtype=np.uint16)
+        grad_dtype = grad_dtype or dtype
+        x = np.empty((n, xc), dtype=storage_numpy_dtype(dtype))
+        gy = np.empty((n, gc), dtype=storage_numpy_dtype(grad_dtype))
         special = np.array(self.x_special_values, dtype=np.float32)
 
         def rng(kind: int, chunk: int) -> np.random.Generator:
@@ -113,8 +140,8 @@ class Workload:
                 g = rng(1, chunk)
                 hit = g.random((m, xc), dtype=np.float32) < np.float32(self.x_special_frac)
                 xf[hit] = special[g.integers(0, len(special), size=int(hit.sum()))]
-            x[r0:r0 + m] = _to_bf16_bits(xf)
-            gy[r0:r0 + m] = _to_bf16_bits(rng(2, chunk).standard_normal((m, gc), dtype=np.float32))
+            x[r0:r0 + m] = _to_storage(xf, dtype)
+            gy[r0:r0 + m] = _to_storage(rng(2, chunk).standard_normal((m, gc), dtype=np.float32), grad_dtype)
 
         chunks = range((n + CHUNK_ROWS - 1) // CHUNK_ROWS)
         workers = threads or max(1, min(16, os.cpu_count() or 1))

@@ -28,8 +28,8 @@
  *        fp32 probs [rows, 1]; fp32 math with the result rounded to x's
  *        dtype; the backward writes d_gate / d_up into the two halves of
  *        grad_x and reduces one probability gradient per row; clamp
- *        gradients follow torch.clamp, i.e. inclusive range masks taken on
- *        the input values.
+ *        gradients follow torch.clamp: the mask is taken on the input
+ *        values and includes the clamp bounds.
  *   [RW] nemo_automodel.components.moe.optimized_ops,
  *        _RouterWeightMulFunction class description and the _rw_fwd_core,
  *        _rw_bwd_x_core and _rw_bwd_probs_core entries: out = (x * probs)
@@ -212,8 +212,8 @@ void oracle_router_weight_mul_bwd(const uint16_t *grad_out, const uint16_t *x, c
  * [SW] lists bfloat16, float16 and float32 as the supported dtypes of x (the
  * _SUPPORTED_DTYPES entry); [RW] lets the router multiply's output be the
  * activation dtype or float32 (the out_dtype parameter of
- * _RouterWeightMulFunction.forward, "fp32 for the scatter-add reduction
- * path"). The math is the same binary32 chain; only loading and the final
+ * _RouterWeightMulFunction.forward, where float32 serves the path that
+ * reduces expert outputs by scatter-add). The math is the same binary32 chain; only loading and the final
  * rounding depend on the dtype. Codes: 0 bfloat16, 1 float16, 2 float32.
  */
 enum { ORACLE_BF16 = 0, ORACLE_F16 = 1, ORACLE_F32 = 2 };

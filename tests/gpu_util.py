@@ -15,7 +15,7 @@ The bar (clamped SwiGLU and router multiply):
 import numpy as np
 import torch
 
-from tests.numerics import bf16_is_nan, bf16_ulp_diff
+from tests.numerics import bf16_is_nan, bf16_ulp_diff, f16_is_nan
 
 DPROBS_REL = 2e-5
 
@@ -32,9 +32,10 @@ def to_host_bits(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def assert_bf16_parity(got: np.ndarray, want: np.ndarray, what: str, exact: bool = False) -> dict:
+def assert_bf16_parity(got: np.ndarray, want: np.ndarray, what: str, exact: bool = False,
+                       is_nan=bf16_is_nan) -> dict:
     assert got.shape == want.shape, (what, got.shape, want.shape)
-    nan_w, nan_g = bf16_is_nan(want), bf16_is_nan(got)
+    nan_w, nan_g = is_nan(want), is_nan(got)
     assert np.array_equal(nan_w, nan_g), f"{what}: NaN positions differ ({int((nan_w != nan_g).sum())})"
     ok = ~nan_w
     g, w = got[ok], want[ok]
@@ -61,3 +62,58 @@ def assert_dprobs(got: np.ndarray, want: np.ndarray, abs_sum: np.ndarray, what: 
     return {"max_err_over_scale": float((err / np.maximum(abs_sum, 1e-30)).max(initial=0)),
             "plain_rel_p50": float(np.median(rel)) if rel.size else 0.0,
             "plain_rel_max": float(rel.max(initial=0))}
+
+
+# ---- float16 / float32 storage -------------------------------------------------
+#
+# float16 outputs: the bfloat16 bar with float16 ulps (1 ulp, zeros bit-exact).
+# float32 outputs: no rounding hides the difference between the kernels'
+# exp (v_exp_f32 of -z*log2(e), whose argument rounding is worth up to |z|
+# ulps of e^-z and so of sigma) and reciprocal (v_rcp_f32) and the oracle's
+# expf and division; every other step is the same binary32 operation in the
+# same order. The oracle is within 8 ulps (y, d_up) or (|gc| + 8) ulps of the
+# scale M = |t*uc|*s*(1 + |gc|*(1-s)) (d_gate) of the exact value, the kernels
+# add |gc| + 8 ulps of sigma's error, carried through (1-s)*gc once more for
+# d_gate. Bar: y, d_up within (|gc| + 16) * 2^-24 * |oracle|; d_gate within
+# (3*|gc| + 16) * 2^-24 * M; zeros bit-exact.
+
+def f16_bits(a) -> np.ndarray:
+    return np.asarray(a).view(np.uint16)
+
+
+def assert_f16_parity(got: np.ndarray, want: np.ndarray, what: str) -> dict:
+    # Same sign-magnitude ulp order as bfloat16; only the NaN encoding differs.
+    return assert_bf16_parity(f16_bits(got), f16_bits(want), what, is_nan=f16_is_nan)
+
+
+def f32_swiglu_bounds(x: np.ndarray, probs: np.ndarray, grad_y: np.ndarray, L: float):
+    """Per-element allowed |gpu - oracle| for y, d_gate and d_up (float32 storage)."""
+    inter = x.shape[1] // 2
+    g = x[:, :inter].astype(np.float64)
+    u = x[:, inter:].astype(np.float64)
+    gc = np.minimum(g, L)
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-gc))
+    uc = np.clip(u, -L, L)
+    p = probs.astype(np.float64)[:, None]
+    a = np.abs(gc * s)
+    eps = 2.0 ** -24
+    y_abs = a * np.abs(uc) * np.abs(p)
+    t = np.abs(grad_y.astype(np.float64) * p)
+    m = t * np.abs(uc) * s * (1 + np.abs(gc) * (1 - s))
+    b_y = (np.abs(gc) + 16) * eps * y_abs + 1e-37
+    b_dg = (3 * np.abs(gc) + 16) * eps * m + 1e-37
+    b_du = (np.abs(gc) + 16) * eps * t * a + 1e-37
+    return b_y, b_dg, b_du
+
+
+def assert_f32_within(got: np.ndarray, want: np.ndarray, bound: np.ndarray, what: str) -> dict:
+    nan_w, nan_g = np.isnan(want), np.isnan(got)
+    assert np.array_equal(nan_w, nan_g), f"{what}: NaN positions differ"
+    ok = ~nan_w
+    zero = ok & (want == 0)
+    assert np.array_equal(got[zero].view(np.uint32), want[zero].view(np.uint32)), f"{what}: zeros differ"
+    err = np.abs(got[ok].astype(np.float64) - want[ok].astype(np.float64))
+    bad = err > bound[ok]
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond the float32 bound"
+    return {"max_err_over_bound": float((err / bound[ok]).max(initial=0)), "exact": float((err == 0).mean())}

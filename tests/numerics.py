@@ -79,6 +79,11 @@ def bf16_is_nan(b) -> np.ndarray:
     return ((b & 0x7F80) == 0x7F80) & ((b & 0x007F) != 0)
 
 
+def f16_is_nan(b) -> np.ndarray:
+    b = np.asarray(b, dtype=np.uint16)
+    return ((b & 0x7C00) == 0x7C00) & ((b & 0x03FF) != 0)
+
+
 def f32_ulp(x) -> np.ndarray:
     """Size of one float32 ulp at |x|."""
     x = np.abs(np.asarray(x, dtype=np.float32))

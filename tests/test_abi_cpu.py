@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # case that passed validation would launch on fake addresses), so skip there.
 pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0, reason="host-only checks; a GPU is visible")
 
-OK, NULLP, SHAPE, LIMIT, ALIAS, MISAL, LAUNCH = range(7)
+OK, NULLP, SHAPE, LIMIT, ALIAS, MISAL, LAUNCH, DTYPE = range(8)
 
 
 @pytest.fixture(scope="module")
@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for code in range(7):
+    for code in range(8):
         s = binding.describe(code)
         assert s and s != "unknown status"
     assert binding.describe(99) == "unknown status"
@@ -128,6 +128,27 @@ def test_router_validation(L):
     assert b(None, None, None, None, None, rows=0) == OK
 
 
+def test_typed_validation(L):
+    sf = lambda x, p, y, dt, rows=4, inter=8: L.swiglu_clamped_fwd_typed(x, p, y, rows, inter, 7.0, dt, None)
+    sb = lambda dt: L.swiglu_clamped_bwd_typed(A, B, C, D, E, 4, 8, 7.0, dt, None)
+    rf = lambda xd, od: L.router_weight_mul_fwd_typed(A, xd, B, C, od, 4, 8, None)
+    rb = lambda od, xd: L.router_weight_mul_bwd_typed(A, od, B, xd, C, D, E, 4, 8, None)
+    for bad in (-1, 3, 99):
+        assert sf(A, B, C, bad) == DTYPE
+        assert sb(bad) == DTYPE
+        assert rf(bad, 0) == DTYPE and rf(0, bad) == DTYPE
+        assert rb(bad, 0) == DTYPE and rb(0, bad) == DTYPE
+    # the output is x's dtype or float32: other pairs are rejected
+    for xd, od in ((2, 0), (2, 1), (0, 1), (1, 0)):
+        assert rf(xd, od) == DTYPE and rb(od, xd) == DTYPE
+    # float32 elements need 4-byte alignment
+    assert sf(A + 2, B, C, 2) == MISAL
+    assert sf(A, B, C + 2, 2) == MISAL
+    # float32 byte sizes double: y at 64 bytes into a 4 x 16 float32 x (256 bytes) overlaps
+    assert sf(A, B, A + 192, 2) == ALIAS
+    assert sf(None, None, None, 2, rows=0) == OK
+
+
 def test_binding_rejects_cpu_tensors_before_the_library():
     x = torch.zeros(4, 16, dtype=torch.bfloat16)
     p = torch.zeros(4, dtype=torch.float32)
@@ -135,6 +156,6 @@ def test_binding_rejects_cpu_tensors_before_the_library():
     with pytest.raises(ValueError):
         binding.swiglu_clamped_fwd(x, p, y, 7.0)
     with pytest.raises(TypeError):
-        binding.swiglu_clamped_fwd(x.float(), p, y, 7.0)
+        binding.swiglu_clamped_fwd(x.double(), p, y, 7.0)
     with pytest.raises(ValueError):
         binding.router_weight_mul_fwd(x[:, :7], p, y[:, :7])

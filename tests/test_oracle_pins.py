@@ -452,7 +452,7 @@ def _router_inputs(rows, hidden, seed):
 
 
 def test_router_fwd_bitwise_equals_eager_fp32_multiply(o):
-    # The pages: the forward is bitwise-identical to (x.float() * probs.float()).to(dtype).
+    # The page states that this forward equals the eager (x.float() * probs.float()).to(dtype) bit for bit.
     d = _router_inputs(96, 7168, 31)
     out = o.router_weight_mul_fwd(d["x"], d["probs"], 96, 7168)
     xt = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16)

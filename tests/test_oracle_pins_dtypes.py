@@ -2,8 +2,8 @@
 
 Pages: nemo_automodel.components.moe.swiglu_triton (_SUPPORTED_DTYPES: bf16,
 fp16, fp32 for x) and nemo_automodel.components.moe.optimized_ops
-(_RouterWeightMulFunction.forward: out_dtype is the activation dtype or fp32
-for the scatter-add reduction path).
+(_RouterWeightMulFunction.forward: out_dtype may be the activation dtype, or
+float32 where expert outputs are combined by scatter-add).
 
 Anchors: numpy's float16 conversions (library routines), float64 torch.clamp /
 F.silu / autograd, torch eager fp32 multiplies, exact rational sums.
