@@ -310,18 +310,6 @@ __device__ __forceinline__ float row_sum(float v, float* part) {
 // for W wavefronts per row), each lane handles V 16-byte vectors per pass over
 // the row (the kernels loop over passes, so any V covers any row), and blocks
 // have B threads (B / G rows per block).
-struct Shape {
-    int G, V, B;
-};
-
-inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-inline int pow2_ceil(int64_t v) {
-    int p = 1;
-    while (p < v) p <<= 1;
-    return p;
-}
-
 // Lanes per row for rows narrower than a wavefront.
 inline int small_group(int64_t nvec) { return nvec > 16 ? 32 : (nvec > 8 ? 16 : 8); }
 

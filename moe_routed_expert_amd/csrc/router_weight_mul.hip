@@ -170,15 +170,27 @@ __global__ __launch_bounds__(kBlock) void router_weight_mul_bwd_scalar_kernel(
     }
 }
 
-// Shapes (measured on MI355X at 65536 x 7168 bf16; nontemporal accesses):
-//   forward:  2 wavefronts per row, 256-thread blocks, up to 16 vectors per
-//             lane per pass (7168: 7 per lane, the whole row in one pass);
-//   backward: 2 vectors per lane and as many wavefronts per row as that needs
-//             (7168: 7 wavefronts), two rows per block where that fits in 1024
-//             threads. Against one wavefront per row (14 vectors per lane) the
-//             forward ran 2% and the backward 8% faster: a row's loads are
-//             issued from several SIMDs at once.
-//   The same shapes serve every dtype (they count elements).
+// Launch shapes: G lanes per row, V vectors per lane per pass, B threads per
+// block (B / G rows per block). For rows of 192 to 1024 vectors (1536 to 8192
+// columns) they come from a sweep on MI355X of 59 forward and 40 backward
+// shapes per dtype pair at 2048, 4096 and 7168 columns (131072, 65536 and
+// 65536 rows), one table per class of pair (16-bit x and output; 16-bit x
+// with float32 output; float32 both): each entry is the shape whose worst
+// case over the pairs sharing it was best, every entry within 2.5% of that
+// case's fastest shape (the shapes they replace lost up to 15%). As for the
+// SwiGLU kernels, one row per block and few rows in flight per CU, each
+// streamed by many wavefronts, did best. Narrower rows keep the earlier rules
+// (a wavefront or less per row under 64 vectors, then 1-2 wavefronts), and so
+// do wider ones (the forward with 2 wavefronts per row and up to 16 vectors
+// per lane, the backward with 2 vectors per lane and up to 16 wavefronts per
+// row; longer rows take several passes).
+enum class Cls { k16, kMixed, k32 };
+
+template <int TX, int TO>
+constexpr Cls cls_of() {
+    return TX == MOE_EPI_F32 ? Cls::k32 : (TO == MOE_EPI_F32 ? Cls::kMixed : Cls::k16);
+}
+
 template <int TX, int TO, int G, int V, int B>
 void launch_fwd(const void* x, const float* probs, void* out, int64_t rows, int64_t hidden, hipStream_t st) {
     hipLaunchKernelGGL((router_weight_mul_fwd_kernel<TX, TO, G, V, B>), dim3(grid_for_rows(rows, B / G)), dim3(B), 0,
@@ -208,17 +220,26 @@ void dispatch_fwd(const void* x, const float* probs, void* out, int64_t rows, in
         }
     }
     if (nvec < 128) return launch_fwd<TX, TO, 64, 2, 256>(x, probs, out, rows, hidden, st);
-    switch (ceil_div(nvec, 128)) {  // vectors per lane with 128 lanes per row
-        case 1: return launch_fwd<TX, TO, 128, 1, 256>(x, probs, out, rows, hidden, st);
-        case 2: return launch_fwd<TX, TO, 128, 2, 256>(x, probs, out, rows, hidden, st);
-        case 3: return launch_fwd<TX, TO, 128, 3, 256>(x, probs, out, rows, hidden, st);
-        case 4: return launch_fwd<TX, TO, 128, 4, 256>(x, probs, out, rows, hidden, st);
-        case 5: case 6: return launch_fwd<TX, TO, 128, 6, 256>(x, probs, out, rows, hidden, st);
-        case 7: return launch_fwd<TX, TO, 128, 7, 256>(x, probs, out, rows, hidden, st);
-        case 8: return launch_fwd<TX, TO, 128, 8, 256>(x, probs, out, rows, hidden, st);
-        case 9: case 10: case 11: case 12: return launch_fwd<TX, TO, 128, 12, 256>(x, probs, out, rows, hidden, st);
-        default: return launch_fwd<TX, TO, 128, 16, 256>(x, probs, out, rows, hidden, st);  // wider rows: passes
+    if (nvec == 128) return launch_fwd<TX, TO, 128, 1, 256>(x, probs, out, rows, hidden, st);
+    if (nvec < 192) return launch_fwd<TX, TO, 128, 2, 256>(x, probs, out, rows, hidden, st);
+    if (nvec <= 1024) {
+        constexpr Cls c = cls_of<TX, TO>();
+        if constexpr (c == Cls::k16) {
+            if (nvec <= 256) return launch_fwd<TX, TO, 192, 1, 192>(x, probs, out, rows, hidden, st);
+            if (nvec <= 512) return launch_fwd<TX, TO, 192, 2, 384>(x, probs, out, rows, hidden, st);
+            return launch_fwd<TX, TO, 320, 2, 320>(x, probs, out, rows, hidden, st);
+        } else if constexpr (c == Cls::kMixed) {
+            if (nvec <= 256) return launch_fwd<TX, TO, 640, 1, 640>(x, probs, out, rows, hidden, st);
+            if (nvec <= 512) return launch_fwd<TX, TO, 896, 2, 896>(x, probs, out, rows, hidden, st);
+            return launch_fwd<TX, TO, 512, 1, 512>(x, probs, out, rows, hidden, st);
+        } else {
+            if (nvec <= 256) return launch_fwd<TX, TO, 1024, 1, 1024>(x, probs, out, rows, hidden, st);
+            if (nvec <= 512) return launch_fwd<TX, TO, 384, 1, 384>(x, probs, out, rows, hidden, st);
+            return launch_fwd<TX, TO, 512, 1, 1024>(x, probs, out, rows, hidden, st);
+        }
     }
+    if (nvec <= 12 * 128) return launch_fwd<TX, TO, 128, 12, 256>(x, probs, out, rows, hidden, st);
+    return launch_fwd<TX, TO, 128, 16, 256>(x, probs, out, rows, hidden, st);  // wider rows: passes
 }
 
 template <int TX, int TO>
@@ -232,18 +253,26 @@ void dispatch_bwd(const void* go, const void* x, const float* probs, void* gx, f
             default: return launch_bwd<TX, TO, 32, 1, 256>(go, x, probs, gx, gp, rows, hidden, st);
         }
     }
-    switch (ceil_div(nvec, 128)) {  // wavefronts per row with 2 vectors per lane
-        case 1: return launch_bwd<TX, TO, 64, 2, 128>(go, x, probs, gx, gp, rows, hidden, st);
-        case 2: return launch_bwd<TX, TO, 128, 2, 256>(go, x, probs, gx, gp, rows, hidden, st);
-        case 3: return launch_bwd<TX, TO, 192, 2, 384>(go, x, probs, gx, gp, rows, hidden, st);
-        case 4: return launch_bwd<TX, TO, 256, 2, 512>(go, x, probs, gx, gp, rows, hidden, st);
-        case 5: return launch_bwd<TX, TO, 320, 2, 640>(go, x, probs, gx, gp, rows, hidden, st);
-        case 6: return launch_bwd<TX, TO, 384, 2, 768>(go, x, probs, gx, gp, rows, hidden, st);
-        case 7: return launch_bwd<TX, TO, 448, 2, 896>(go, x, probs, gx, gp, rows, hidden, st);
-        case 8: return launch_bwd<TX, TO, 512, 2, 1024>(go, x, probs, gx, gp, rows, hidden, st);
-        case 9: case 10: case 11: case 12: return launch_bwd<TX, TO, 768, 2, 768>(go, x, probs, gx, gp, rows, hidden, st);
-        default: return launch_bwd<TX, TO, 1024, 2, 1024>(go, x, probs, gx, gp, rows, hidden, st);  // wider: passes
+    if (nvec <= 128) return launch_bwd<TX, TO, 64, 2, 128>(go, x, probs, gx, gp, rows, hidden, st);
+    if (nvec < 192) return launch_bwd<TX, TO, 128, 2, 256>(go, x, probs, gx, gp, rows, hidden, st);
+    if (nvec <= 1024) {
+        constexpr Cls c = cls_of<TX, TO>();
+        if constexpr (c == Cls::k16) {
+            if (nvec <= 256) return launch_bwd<TX, TO, 256, 2, 512>(go, x, probs, gx, gp, rows, hidden, st);
+            if (nvec <= 512) return launch_bwd<TX, TO, 512, 2, 1024>(go, x, probs, gx, gp, rows, hidden, st);
+            return launch_bwd<TX, TO, 448, 2, 896>(go, x, probs, gx, gp, rows, hidden, st);
+        } else if constexpr (c == Cls::kMixed) {
+            if (nvec <= 256) return launch_bwd<TX, TO, 320, 1, 640>(go, x, probs, gx, gp, rows, hidden, st);
+            if (nvec <= 512) return launch_bwd<TX, TO, 512, 2, 1024>(go, x, probs, gx, gp, rows, hidden, st);
+            return launch_bwd<TX, TO, 896, 1, 896>(go, x, probs, gx, gp, rows, hidden, st);
+        } else {
+            if (nvec <= 256) return launch_bwd<TX, TO, 512, 1, 1024>(go, x, probs, gx, gp, rows, hidden, st);
+            if (nvec <= 512) return launch_bwd<TX, TO, 896, 1, 896>(go, x, probs, gx, gp, rows, hidden, st);
+            return launch_bwd<TX, TO, 896, 2, 896>(go, x, probs, gx, gp, rows, hidden, st);
+        }
     }
+    if (nvec <= 12 * 128) return launch_bwd<TX, TO, 768, 2, 768>(go, x, probs, gx, gp, rows, hidden, st);
+    return launch_bwd<TX, TO, 1024, 2, 1024>(go, x, probs, gx, gp, rows, hidden, st);  // wider rows: passes
 }
 
 // The (x, output) dtype pairs: the output is x's dtype or float32.

@@ -243,16 +243,23 @@ __global__ __launch_bounds__(kBwdBlock) void swiglu_clamped_bwd_scalar_kernel(
 
 // ---- launchers ---------------------------------------------------------------
 //
-// Shapes (measured on MI355X at 131072 x 2048 bf16; nontemporal accesses):
-//   forward:  one vector per lane (V = 1) and up to 4 wavefronts per row,
-//             256-thread blocks (inter = 2048: 4 wavefronts, one row per block);
-//   backward: two vectors per lane (V = 2) and as many wavefronts per row as
-//             that needs (up to 8), two rows per block (inter = 2048: 2
-//             wavefronts per row, 256-thread blocks). Splitting a row over
-//             several wavefronts issues its loads from several SIMDs at once;
-//             these shapes ran 1-1.5% faster than one wavefront per row.
-//   Rows longer than the shape covers take several passes (V is capped).
-//   The same shapes serve every dtype (they count elements).
+// Launch shapes: G lanes per row, V vectors per lane per pass, B threads per
+// block (B / G rows per block). For rows of 192 vectors (1536 columns) and
+// more they come from a sweep on MI355X of 59 forward and 40 backward shapes
+// per dtype at 1536, 2048, 4096 and 8192 columns (100003, 131072, 65536 and
+// 32768 rows), one table per element width: each entry is the shape whose
+// worst case over the dtypes sharing it was best, and every entry was within
+// 2.5% of that case's fastest shape (the shapes they replace lost up to 16%).
+// What the sweep showed:
+//  - one row per block beats two in the backward (the row sum's barrier then
+//    holds only that row's waves);
+//  - the best shapes keep few rows in flight per CU, each streamed by many
+//    wavefronts, even where that leaves lanes idle (448 lanes for 192 float32
+//    vectors): fewer, longer runs per DRAM page;
+//  - float32 wants more lanes per row than 16-bit types at the same width.
+// Narrower rows keep the earlier rules (a wavefront or less per row for
+// under 64 vectors, up to 4 wavefronts between 64 and 191). Rows wider than a
+// shape covers take several passes.
 
 template <int T, int G, int V, int B>
 void launch_fwd(const void* x, const float* probs, void* y, int64_t rows, int64_t inter, float L, hipStream_t st) {
@@ -272,58 +279,52 @@ void launch_bwd(const void* x, const float* probs, const void* gy, void* gx, flo
                            rows, inter, L);
 }
 
-Shape fwd_shape(int64_t nvec) {
-    if (nvec < 64) return Shape{small_group(nvec), 1, 256};
-    const int w = pow2_ceil(ceil_div(nvec, 64)) > 4 ? 4 : pow2_ceil(ceil_div(nvec, 64));
-    const int64_t v = ceil_div(nvec, 64 * w);
-    return Shape{64 * w, static_cast<int>(v > 4 ? 4 : v), 256};
-}
-
-Shape bwd_shape(int64_t nvec) {
-    if (nvec < 64) return Shape{small_group(nvec), 1, 128};
-    if (nvec <= 128) return Shape{64, static_cast<int>(ceil_div(nvec, 64)), 128};
-    const int w = pow2_ceil(ceil_div(nvec, 128)) > 8 ? 8 : pow2_ceil(ceil_div(nvec, 128));
-    // V is capped at 2: with 1024-thread blocks more float32 vectors would
-    // exceed the register budget (wider rows take more passes instead)
-    const int64_t v = ceil_div(nvec, 64 * w);
-    return Shape{64 * w, static_cast<int>(v > 2 ? 2 : v), 2 * 64 * w > 1024 ? 1024 : 2 * 64 * w};
-}
-
 template <int T>
 void dispatch_fwd(const void* x, const float* probs, void* y, int64_t rows, int64_t inter, float L, hipStream_t st) {
-    const Shape sh = fwd_shape(inter / 8);
-    switch (sh.G * 8 + sh.V) {
-        case 8 * 8 + 1: return launch_fwd<T, 8, 1, 256>(x, probs, y, rows, inter, L, st);
-        case 16 * 8 + 1: return launch_fwd<T, 16, 1, 256>(x, probs, y, rows, inter, L, st);
-        case 32 * 8 + 1: return launch_fwd<T, 32, 1, 256>(x, probs, y, rows, inter, L, st);
-        case 64 * 8 + 1: return launch_fwd<T, 64, 1, 256>(x, probs, y, rows, inter, L, st);
-        case 128 * 8 + 1: return launch_fwd<T, 128, 1, 256>(x, probs, y, rows, inter, L, st);
-        case 256 * 8 + 1: return launch_fwd<T, 256, 1, 256>(x, probs, y, rows, inter, L, st);
-        case 256 * 8 + 2: return launch_fwd<T, 256, 2, 256>(x, probs, y, rows, inter, L, st);
-        case 256 * 8 + 3: return launch_fwd<T, 256, 3, 256>(x, probs, y, rows, inter, L, st);
-        default: return launch_fwd<T, 256, 4, 256>(x, probs, y, rows, inter, L, st);
+    const int64_t nvec = inter / 8;
+    if (nvec < 64) {
+        switch (small_group(nvec)) {
+            case 8: return launch_fwd<T, 8, 1, 256>(x, probs, y, rows, inter, L, st);
+            case 16: return launch_fwd<T, 16, 1, 256>(x, probs, y, rows, inter, L, st);
+            default: return launch_fwd<T, 32, 1, 256>(x, probs, y, rows, inter, L, st);
+        }
+    }
+    if (nvec == 64) return launch_fwd<T, 64, 1, 256>(x, probs, y, rows, inter, L, st);
+    if (nvec <= 128) return launch_fwd<T, 128, 1, 256>(x, probs, y, rows, inter, L, st);
+    if (nvec < 192) return launch_fwd<T, 256, 1, 256>(x, probs, y, rows, inter, L, st);
+    if constexpr (T == MOE_EPI_F32) {
+        if (nvec <= 512) return launch_fwd<T, 448, 4, 448>(x, probs, y, rows, inter, L, st);
+        return launch_fwd<T, 384, 1, 384>(x, probs, y, rows, inter, L, st);
+    } else {
+        if (nvec == 192) return launch_fwd<T, 256, 1, 512>(x, probs, y, rows, inter, L, st);
+        if (nvec <= 256) return launch_fwd<T, 256, 1, 256>(x, probs, y, rows, inter, L, st);
+        return launch_fwd<T, 1024, 1, 1024>(x, probs, y, rows, inter, L, st);
     }
 }
 
 template <int T>
 void dispatch_bwd(const void* x, const float* probs, const void* gy, void* gx, float* gp, int64_t rows, int64_t inter,
                   float L, hipStream_t st) {
-    const Shape sh = bwd_shape(inter / 8);
-    switch (sh.G * 8 + sh.V) {
-        case 8 * 8 + 1: return launch_bwd<T, 8, 1, 128>(x, probs, gy, gx, gp, rows, inter, L, st);
-        case 16 * 8 + 1: return launch_bwd<T, 16, 1, 128>(x, probs, gy, gx, gp, rows, inter, L, st);
-        case 32 * 8 + 1: return launch_bwd<T, 32, 1, 128>(x, probs, gy, gx, gp, rows, inter, L, st);
-        case 64 * 8 + 1: return launch_bwd<T, 64, 1, 128>(x, probs, gy, gx, gp, rows, inter, L, st);
-        case 64 * 8 + 2: return launch_bwd<T, 64, 2, 128>(x, probs, gy, gx, gp, rows, inter, L, st);
-        case 128 * 8 + 2: return launch_bwd<T, 128, 2, 256>(x, probs, gy, gx, gp, rows, inter, L, st);
-        case 256 * 8 + 2: return launch_bwd<T, 256, 2, 512>(x, probs, gy, gx, gp, rows, inter, L, st);
-        default:
-            // float32 rows this wide carry 96 bytes per vector triple: one row per
-            // block keeps two blocks per CU within the register budget unspilled
-            if constexpr (T == MOE_EPI_F32)
-                return launch_bwd<T, 512, 2, 512>(x, probs, gy, gx, gp, rows, inter, L, st);
-            else
-                return launch_bwd<T, 512, 2, 1024>(x, probs, gy, gx, gp, rows, inter, L, st);
+    const int64_t nvec = inter / 8;
+    if (nvec < 64) {
+        switch (small_group(nvec)) {
+            case 8: return launch_bwd<T, 8, 1, 128>(x, probs, gy, gx, gp, rows, inter, L, st);
+            case 16: return launch_bwd<T, 16, 1, 128>(x, probs, gy, gx, gp, rows, inter, L, st);
+            default: return launch_bwd<T, 32, 1, 128>(x, probs, gy, gx, gp, rows, inter, L, st);
+        }
+    }
+    if (nvec == 64) return launch_bwd<T, 64, 1, 128>(x, probs, gy, gx, gp, rows, inter, L, st);
+    if (nvec <= 128) return launch_bwd<T, 64, 2, 128>(x, probs, gy, gx, gp, rows, inter, L, st);
+    if (nvec < 192) return launch_bwd<T, 128, 2, 256>(x, probs, gy, gx, gp, rows, inter, L, st);
+    if constexpr (T == MOE_EPI_F32) {
+        if (nvec <= 256) return launch_bwd<T, 384, 2, 384>(x, probs, gy, gx, gp, rows, inter, L, st);
+        if (nvec <= 512) return launch_bwd<T, 640, 2, 640>(x, probs, gy, gx, gp, rows, inter, L, st);
+        return launch_bwd<T, 512, 1, 1024>(x, probs, gy, gx, gp, rows, inter, L, st);
+    } else {
+        if (nvec == 192) return launch_bwd<T, 256, 1, 512>(x, probs, gy, gx, gp, rows, inter, L, st);
+        if (nvec <= 256) return launch_bwd<T, 192, 1, 384>(x, probs, gy, gx, gp, rows, inter, L, st);
+        if (nvec <= 512) return launch_bwd<T, 448, 1, 448>(x, probs, gy, gx, gp, rows, inter, L, st);
+        return launch_bwd<T, 512, 2, 512>(x, probs, gy, gx, gp, rows, inter, L, st);
     }
 }
 

@@ -148,11 +148,12 @@ def _offset_view(bits: np.ndarray, offset_elems: int) -> torch.Tensor:
     return view.view(*bits.shape)
 
 
-# every lane-group width (8, 16, 32, 64), every vectors-per-lane count the
-# SwiGLU kernels use (1-4), multi-pass rows (2056, 4096, 8200), ragged row
-# counts, and the per-element path (odd widths; offset pointers)
+# Row widths reach every launch-shape bucket (vectors of 8 per row: < 64 with lane groups of 8, 16 and 32; 64;
+# 65-128; 129-191; 192; 193-256; 257-512; 513-1024; wider, in several passes), with ragged row counts, and the
+# per-element path (widths not a multiple of 8; offset pointers).
 SHAPES = [(1, 1), (3, 3), (2, 8), (37, 8), (5, 24), (64, 56), (33, 64), (17, 136), (9, 200), (40, 520),
-          (7, 1544), (5, 2056), (1031, 128), (300, 1536), (129, 2048), (11, 4096), (3, 8200), (6, 1032)]
+          (7, 1544), (5, 2056), (1031, 128), (300, 1536), (129, 2048), (11, 4096), (3, 8200), (6, 1032),
+          (4, 6144), (2, 16384), (5, 512), (3, 3072)]
 
 
 @pytest.mark.parametrize("rows,inter", SHAPES)
@@ -179,7 +180,9 @@ def test_swiglu_shapes_and_alignment(rows, inter, offset):
 # hidden 4096/5120/6144/7168/8192 use 8/10/12/14/16 vectors per lane in one
 # pass, 7176 rounds 15 up to 16, 16384 takes two passes of 16
 @pytest.mark.parametrize("rows,hidden", [(1, 1), (3, 7), (13, 8), (64, 24), (9, 1000), (257, 7168), (31, 7176),
-                                         (19, 4096), (7, 5120), (5, 6144), (9, 8192), (3, 16384), (4, 200)])
+                                         (19, 4096), (7, 5120), (5, 6144), (9, 8192), (3, 16384), (4, 200),
+                                         (7, 1536), (6, 1544), (33, 2048), (5, 2056), (3, 3072), (2, 1040),
+                                         (4, 12288), (3, 1024)])
 @pytest.mark.parametrize("offset", [0, 1])
 def test_router_shapes_and_alignment(rows, hidden, offset):
     d = custom("router", rows, hidden, x_sigma=1.0, seed=2000 + rows * 3 + hidden).generate()
