@@ -77,7 +77,7 @@ struct Quads {
 };
 
 template <int G, bool kSplit>
-__device__ __forceinline__ Quads quads_of(uint32_t c, uint32_t lane, uint32_t nvec) {
+__host__ __device__ __forceinline__ Quads quads_of(uint32_t c, uint32_t lane, uint32_t nvec) {
     if constexpr (kSplit) {
         const uint32_t base = c - lane;  // first vector of this chunk
         const uint32_t n = nvec - base < static_cast<uint32_t>(G) ? nvec - base : static_cast<uint32_t>(G);
