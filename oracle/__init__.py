@@ -256,3 +256,57 @@ def router_weight_mul_bwd_typed(grad_out, go_dtype, x, x_dtype, probs, rows, hid
     if with_abs_sum:
         return grad_x, grad_probs, abs_sum
     return grad_x, grad_probs
+
+
+# ---- gate_up grouped GEMM with the clamped SwiGLU epilogue ----------------
+
+def _grouped_lib():
+    lib = _load()
+    if not getattr(lib, "_grouped_ready", False):
+        vp = ctypes.c_void_p
+        lib.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
+        lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
+        lib.oracle_grouped_gate_up.argtypes = [vp, vp, vp, vp, vp, vp, _i64, _i64, _i64, _i64, ctypes.c_int]
+        lib.oracle_grouped_gate_up.restype = None
+        lib.oracle_grouped_swiglu_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, _i64, _i64, _i64, _i64,
+                                                  ctypes.c_float, ctypes.c_int]
+        lib.oracle_grouped_swiglu_fwd.restype = None
+        lib._grouped_ready = True
+    return lib
+
+
+def f64_to_bf16(v: float) -> int:
+    return int(_grouped_lib().oracle_f64_to_bf16(float(v)))
+
+
+def grouped_gate_up(a, w_gate, w_up, offs, tokens, hidden, inter, experts, with_abs_sum=False, threads=None):
+    """Exact grouped sums [tokens, 2*inter] (float64; rows of no expert are NaN)[, sum |a*w|].
+    a: [tokens, hidden] bf16 bits; w_gate, w_up: [experts, inter, hidden] bf16 bits; offs: int32 [experts]."""
+    a = _arr(a, np.uint16, (tokens, hidden))
+    w_gate = _arr(w_gate, np.uint16, (experts, inter, hidden))
+    w_up = _arr(w_up, np.uint16, (experts, inter, hidden))
+    offs = _arr(offs, np.int32, (experts,))
+    s = np.full((tokens, 2 * inter), np.nan)
+    s_abs = np.full((tokens, 2 * inter), np.nan) if with_abs_sum else None
+    _grouped_lib().oracle_grouped_gate_up(_vp(a), _vp(w_gate), _vp(w_up), _vp(offs), _vp(s), _vp(s_abs), tokens,
+                                          hidden, inter, experts, threads or default_threads())
+    return (s, s_abs) if with_abs_sum else s
+
+
+def grouped_swiglu_fwd(a, w_gate, w_up, offs, probs, tokens, hidden, inter, experts, L, y_init=None,
+                       x_init=None, threads=None):
+    """(y [tokens, inter], x [tokens, 2*inter]) as bf16 bits. Rows of no expert keep y_init / x_init
+    (default 0xFFFF, a NaN pattern no computed value takes)."""
+    a = _arr(a, np.uint16, (tokens, hidden))
+    w_gate = _arr(w_gate, np.uint16, (experts, inter, hidden))
+    w_up = _arr(w_up, np.uint16, (experts, inter, hidden))
+    offs = _arr(offs, np.int32, (experts,))
+    probs = _arr(probs, np.float32, (tokens,))
+    y = np.array(y_init, dtype=np.uint16) if y_init is not None else np.full((tokens, inter), 0xFFFF, np.uint16)
+    x = np.array(x_init, dtype=np.uint16) if x_init is not None else np.full((tokens, 2 * inter), 0xFFFF,
+                                                                            np.uint16)
+    scratch = np.empty((tokens, 2 * inter), dtype=np.float64)
+    _grouped_lib().oracle_grouped_swiglu_fwd(_vp(a), _vp(w_gate), _vp(w_up), _vp(offs), _vp(probs), _vp(y), _vp(x),
+                                             _vp(scratch), tokens, hidden, inter, experts, float(L),
+                                             threads or default_threads())
+    return y, x

@@ -374,3 +374,139 @@ void oracle_router_weight_mul_bwd_typed(const void *grad_out, int go_dtype, cons
             grad_probs_abs[r] = acc_abs;
     }
 }
+
+/* ---- gate_up grouped GEMM with the clamped SwiGLU epilogue ------------- */
+/*
+ * Sources:
+ *   [MK] nemo_automodel.components.moe.mok_experts, the routed expert weight
+ *        parameters: routed gate and up weights are contiguous bfloat16
+ *        tensors of shape [local_experts, expert_intermediate, hidden].
+ *   [GM] nemo_automodel.components.moe.quantized_experts,
+ *        MXFP4ExpertStorageMixin._mxfp4_base_mm: the routed activations are
+ *        [tokens, in_dim], grouped contiguously by local expert; offs is an
+ *        int32 [local_experts] tensor of cumulative token counts; the result is
+ *        [tokens, out_dim] in the activation dtype.
+ *   [SW] (above): the epilogue consumes that grouped-GEMM output, x = [gate | up].
+ *
+ * Rows of expert e are [start_e, end_e) with start_0 = 0, end_e = offs[e]
+ * clamped to [start_e, tokens] and start_{e+1} = end_e (a count that is
+ * negative, decreasing or past the end gives an empty or shortened range;
+ * rows at or past the last end belong to no expert and are not written).
+ * For such a row t of expert e and column j < inter:
+ *   gate[t, j] = sum_h a[t, h] * w_gate[e, j, h]
+ *   up[t, j]   = sum_h a[t, h] * w_up[e, j, h]
+ * Each product of two bfloat16 values is exact in binary64; the products are
+ * added in binary64 in ascending h, which is exact while the products of a
+ * sum span fewer than about 2^37 in magnitude (true of any data the tests
+ * use). The grouped GEMM's output in the activation dtype is that exact sum
+ * rounded once to bfloat16.
+ */
+
+/* binary64 -> bfloat16, to nearest, ties to even, with subnormals (unit 2^-133),
+ * overflow to infinity and NaN kept NaN. Same method as oracle_f32_to_f16: the
+ * magnitude as an integer multiple n of the bfloat16 unit at its exponent. */
+uint16_t oracle_f64_to_bf16(double v)
+{
+    uint64_t bits;
+    memcpy(&bits, &v, sizeof bits);
+    uint16_t sign = (uint16_t)((bits >> 48) & 0x8000u);
+    int ed = (int)((bits >> 52) & 0x7FFu);
+    uint64_t frac = bits & 0xFFFFFFFFFFFFFull;
+    if (ed == 0x7FF)
+        return (uint16_t)(sign | (frac ? (0x7FC0u | (uint16_t)(frac >> 45)) : 0x7F80u));
+    if (ed == 0)
+        return sign;                                     /* binary64 zero/subnormal: far below 2^-134 */
+    int e = ed - 1023;                                   /* value = m * 2^(e - 52), m in [2^52, 2^53) */
+    uint64_t m = frac | (1ull << 52);
+    int emin = e < -126 ? -126 : e;                      /* bfloat16 exponent used (subnormals: -126) */
+    int sh = (emin - 7) - (e - 52);                      /* value / unit = m / 2^sh, sh >= 45 */
+    uint64_t n, rem, half;
+    if (sh >= 60) {
+        n = 0; rem = m; half = 1ull << 59;               /* m < 2^53: below half a unit */
+    } else {
+        n = m >> sh;
+        rem = m & ((1ull << sh) - 1);
+        half = 1ull << (sh - 1);
+    }
+    if (rem > half || (rem == half && (n & 1u)))
+        n += 1;
+    if (e < -126)
+        return (uint16_t)(sign | n);                     /* subnormal (n == 128 is the smallest normal) */
+    if (e > 127)
+        return (uint16_t)(sign | 0x7F80u);
+    uint32_t out = ((uint32_t)(e + 127) << 7) + (uint32_t)(n - 128); /* n == 256 carries into the exponent */
+    if (out >= 0x7F80u)
+        return (uint16_t)(sign | 0x7F80u);
+    return (uint16_t)(sign | out);
+}
+
+/* [GM][MK] the exact grouped sums. sum is [tokens, 2*inter] (gate in columns
+ * [0, inter), up in [inter, 2*inter)); abs_sum (may be NULL) receives
+ * sum_h |a * w| for each output: the scale of the rounding error of a sum
+ * accumulated in another order or precision. Rows of no expert are not written. */
+void oracle_grouped_gate_up(const uint16_t *a, const uint16_t *w_gate, const uint16_t *w_up,
+                            const int32_t *offs, double *sum, double *abs_sum,
+                            int64_t tokens, int64_t hidden, int64_t inter, int64_t experts, int nthreads)
+{
+    int64_t start = 0;
+    for (int64_t e = 0; e < experts; ++e) {
+        int64_t end = offs[e];
+        if (end < start) end = start;
+        if (end > tokens) end = tokens;
+        int64_t t;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+        for (t = start; t < end; ++t) {
+            const uint16_t *at = a + t * hidden;
+            for (int64_t half = 0; half < 2; ++half) {
+                const uint16_t *w = (half == 0 ? w_gate : w_up) + e * inter * hidden;
+                for (int64_t j = 0; j < inter; ++j) {
+                    const uint16_t *wj = w + j * hidden;
+                    double s = 0.0, s_abs = 0.0;
+                    for (int64_t h = 0; h < hidden; ++h) {
+                        double prod = (double)oracle_bf16_to_f32(at[h]) * (double)oracle_bf16_to_f32(wj[h]);
+                        s += prod;
+                        s_abs += fabs(prod);
+                    }
+                    sum[t * 2 * inter + half * inter + j] = s;
+                    if (abs_sum)
+                        abs_sum[t * 2 * inter + half * inter + j] = s_abs;
+                }
+            }
+        }
+        start = end;
+    }
+}
+
+/* [GM][MK][SW] the fused forward: x = bf16(exact grouped sums) (written to
+ * x_out when it is not NULL, [tokens, 2*inter]), then y = the [SW] forward of
+ * that x ([tokens, inter]). sum_scratch is caller memory of tokens*2*inter
+ * doubles. Rows of no expert are not written. */
+void oracle_grouped_swiglu_fwd(const uint16_t *a, const uint16_t *w_gate, const uint16_t *w_up,
+                               const int32_t *offs, const float *probs, uint16_t *y, uint16_t *x_out,
+                               double *sum_scratch, int64_t tokens, int64_t hidden, int64_t inter,
+                               int64_t experts, float L, int nthreads)
+{
+    oracle_grouped_gate_up(a, w_gate, w_up, offs, sum_scratch, NULL, tokens, hidden, inter, experts, nthreads);
+    int64_t start = 0;
+    for (int64_t e = 0; e < experts; ++e) {
+        int64_t end = offs[e];
+        if (end < start) end = start;
+        if (end > tokens) end = tokens;
+        int64_t t;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+        for (t = start; t < end; ++t) {
+            for (int64_t j = 0; j < inter; ++j) {
+                uint16_t g = oracle_f64_to_bf16(sum_scratch[t * 2 * inter + j]);
+                uint16_t u = oracle_f64_to_bf16(sum_scratch[t * 2 * inter + inter + j]);
+                if (x_out) {
+                    x_out[t * 2 * inter + j] = g;
+                    x_out[t * 2 * inter + inter + j] = u;
+                }
+                float q[4];
+                oracle_swiglu_point(oracle_bf16_to_f32(g), oracle_bf16_to_f32(u), probs[t], 0.0f, L, q);
+                y[t * inter + j] = oracle_f32_to_bf16(q[0]);
+            }
+        }
+        start = end;
+    }
+}

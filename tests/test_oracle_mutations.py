@@ -18,6 +18,7 @@ import oracle as real_oracle
 from oracle import build as oracle_build
 from tests import test_oracle_pins as pins
 from tests import test_oracle_pins_dtypes as dpins
+from tests import test_oracle_pins_grouped as gpins
 
 SRC = oracle_build.SRC
 
@@ -61,6 +62,19 @@ MUTANTS = [
     ("typed router forward skips the probability",
      "oracle_store(out, r * hidden + k, out_dtype, oracle_load(x, r * hidden + k, x_dtype) * probs[r]);",
      "oracle_store(out, r * hidden + k, out_dtype, oracle_load(x, r * hidden + k, x_dtype));"),
+    ("grouped: weights read transposed",
+     "double prod = (double)oracle_bf16_to_f32(at[h]) * (double)oracle_bf16_to_f32(wj[h]);",
+     "double prod = (double)oracle_bf16_to_f32(at[h]) * (double)oracle_bf16_to_f32(w[h * inter + j]);"),
+    ("grouped: the previous expert's weights",
+     "const uint16_t *w = (half == 0 ? w_gate : w_up) + e * inter * hidden;",
+     "const uint16_t *w = (half == 0 ? w_gate : w_up) + (e > 0 ? e - 1 : 0) * inter * hidden;"),
+    ("grouped: gate and up weights swapped",
+     "const uint16_t *w = (half == 0 ? w_gate : w_up) + e * inter * hidden;",
+     "const uint16_t *w = (half == 0 ? w_up : w_gate) + e * inter * hidden;"),
+    ("grouped: offs read as per-expert counts", "int64_t end = offs[e];", "int64_t end = start + offs[e];"),
+    ("grouped: decreasing counts not clamped", "if (end < start) end = start;", ";"),
+    ("grouped: sums rounded through binary32", "uint16_t g = oracle_f64_to_bf16(sum_scratch[t * 2 * inter + j]);",
+     "uint16_t g = oracle_f32_to_bf16((float)sum_scratch[t * 2 * inter + j]);"),
     ("typed backward reads grad_y as x's neighbour",
      "oracle_load(grad_y, r * inter + j, dtype), L, q);", "oracle_load(x, r * inter + j, dtype), L, q);"),
 ]
@@ -96,6 +110,14 @@ def _pins():
                                          for a, b in ((real_oracle.BF16, real_oracle.F32),
                                                       (real_oracle.F16, real_oracle.F16))]),
         ("router fp32 grad_out", lambda o: dpins.test_router_typed_backward_fp32_grad_out(o)),
+        ("binary64 rounding", lambda o: gpins.test_f64_rounding_matches_nearest_search_and_the_exact_helper(o)),
+        ("grouped integer products", lambda o: [gpins.test_integer_products_per_expert_are_exact(f, o) for f in
+                                                ([3, 3, 9, 14], [5, 2, 20, 14], [-4, 6, 9, 11])]),
+        ("grouped float64 matmul", lambda o: gpins.test_float64_matmul_on_normal_data(o)),
+        ("grouped rational sums", lambda o: gpins.test_tiny_case_exact_rational_sums_and_rounding(o)),
+        ("grouped per-expert scale", lambda o: gpins.test_per_expert_power_of_two_weights_select_the_expert(o)),
+        ("grouped epilogue", lambda o: gpins.test_forward_is_the_epilogue_of_the_rounded_sums(o)),
+        ("grouped tie", lambda o: gpins.test_sums_next_to_a_bf16_tie_are_rounded_once(o)),
     ]
     return calls
 
