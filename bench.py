@@ -25,6 +25,12 @@ Prints one JSON line. Options:
   --no-grad-probs    backward without the probability gradient (probabilities
                      that carry no gradient; the router then does not read x)
   --no-cpu-baseline  skip the oracle timing on the host
+  --workload grouped_* the gate_up grouped GEMM with the clamped SwiGLU
+                     epilogue fused into it (one launch per step; x = [gate | up]
+                     is written too, as the backward needs it, unless --no-x):
+                     value in TFLOP/s of the two products, roofline against
+                     the dense bf16 MFMA peak
+  --no-x             grouped: write y only
   --copy-calibration time a 1 GiB device-to-device copy instead (torch's copy_,
                      carried out by the HIP runtime's copy kernel): the plain
                      copy of known size whose FETCH_SIZE / WRITE_SIZE readings
@@ -44,9 +50,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published peak
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published peak (no sparsity)
 METRICS = {
     "swiglu": "achieved HBM GB/s (% of MI355X peak), clamped-SwiGLU fwd+bwd at 131072×4096 bf16",
     "router": "achieved HBM GB/s (% of MI355X peak), fp32 router-weight multiply fwd+bwd",
+    "grouped": "achieved TFLOP/s (% of MI355X dense bf16 peak), gate_up grouped GEMM + clamped SwiGLU epilogue",
 }
 
 
@@ -64,6 +72,7 @@ def parse_args():
                     help="time budget of the oracle baseline: whole-workload passes until it is spent")
     ap.add_argument("--cpu-threads", type=int, default=None)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-x", action="store_true")
     return ap.parse_args()
 
 
@@ -83,13 +92,19 @@ def kernel_source_digest() -> str:
 PROFILE_FOR = {"swiglu": "swiglu_clamped", "router": "router_weight_mul"}
 
 
+def profile_name(workload) -> str:
+    """The committed rocprofv3 summary that covers a workload's kernels."""
+    if hasattr(workload, "experts"):  # the grouped GEMM + epilogue
+        return "grouped_gate_up_swiglu_" + workload.name[len("grouped_"):] + ".md"
+    return f"{PROFILE_FOR[workload.op]}_{workload.rows}x{workload.cols}.md"
+
+
 def load_traffic(kernel: str, workload) -> float | None:
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary profiles/<op>_<rows>x<cols>.md (FETCH_SIZE and WRITE_SIZE, each
+    summary (profile_name; FETCH_SIZE and WRITE_SIZE, each
     scaled by its reading for a device copy of known size). None if there is
     no summary or it was taken on other kernel sources."""
-    name = f"{PROFILE_FOR[workload.op]}_{workload.rows}x{workload.cols}.md"
-    path = os.path.join(ROOT, "profiles", name)
+    path = os.path.join(ROOT, "profiles", profile_name(workload))
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -148,6 +163,9 @@ def main():
     if args.copy_calibration:
         return copy_calibration(args)
 
+    from moe_routed_expert_amd.workloads import GROUPED_WORKLOADS
+    if args.workload in GROUPED_WORKLOADS:
+        return grouped_main(args, GROUPED_WORKLOADS[args.workload])
     w = WORKLOADS[args.workload or HEADLINE]
     dt = args.dtype
     od = (args.out_dtype or dt) if w.op == "router" else dt
@@ -275,6 +293,102 @@ def main():
                    "limit": w.limit, "storage": dt, "output": od, "grad_probs": want_gp,
                    "io": f"{dt} tensors, fp32 probs; fp32 arithmetic", "bytes_per_step": fwd_b + bwd_b},
         "frac_of_peak": value / PEAK_HBM_GBS,
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def grouped_main(args, w):
+    """One step = one fused grouped GEMM + epilogue launch over the whole workload."""
+    import numpy as np
+    import torch
+
+    import moe_routed_expert_amd as epi
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    d = w.generate()
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    a, wg, wu = bf(d["a"]), bf(d["w_gate"]), bf(d["w_up"])
+    offs = torch.from_numpy(d["offs"]).to(dev)
+    p = torch.from_numpy(d["probs"]).to(dev)
+    y = torch.empty((w.tokens, w.inter), dtype=torch.bfloat16, device=dev)
+    x = None if args.no_x else torch.empty((w.tokens, 2 * w.inter), dtype=torch.bfloat16, device=dev)
+    step = lambda: epi.grouped_gate_up_swiglu_fwd(a, wg, wu, offs, p, y, x, w.limit)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    flops = w.flops()
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    avg_ms = float(ms.mean())
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    name = "grouped_gate_up_swiglu_fwd"
+    kernels = {name: {"avg_us": avg_ms * 1e3, "median_us": float(np.median(ms)) * 1e3, "min_us": float(ms.min()) * 1e3,
+                      "flops": flops, "TFLOP/s": achieved, "frac_of_peak": achieved / PEAK_BF16_TFLOPS,
+                      "min_hbm_bytes": w.min_bytes(not args.no_x)}}
+    traffic = None if args.no_x else load_traffic(name, w)
+    roofline = {"bound": "mfma", "kernel": name, "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "flops_per_launch": flops}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = args.cpu_threads or oracle.default_threads()
+        # sample: the first 8 rows of every expert, regrouped with their own counts
+        ends = d["offs"].astype(np.int64)
+        starts = np.concatenate([[0], ends[:-1]])
+        idx = np.concatenate([np.arange(s0, min(s0 + 8, e0)) for s0, e0 in zip(starts, ends)]).astype(np.int64)
+        sub_offs = np.cumsum([min(8, max(0, e0 - s0)) for s0, e0 in zip(starts, ends)]).astype(np.int32)
+        sa, sp = d["a"][idx], d["probs"][idx]
+        print(f"[bench] oracle on the host ({threads} threads): {idx.size} sampled rows per pass for >= "
+              f"{args.cpu_seconds:g} s", file=sys.stderr, flush=True)
+        passes, t = 0, time.perf_counter()
+        while True:
+            oracle.grouped_swiglu_fwd(sa, d["w_gate"], d["w_up"], sub_offs, sp, idx.size, w.hidden, w.inter,
+                                      w.experts, w.limit, threads=threads)
+            passes += 1
+            ct = time.perf_counter() - t
+            if ct >= args.cpu_seconds or passes >= 100:
+                break
+        sample_flops = 2 * idx.size * w.hidden * 2 * w.inter
+        cpu = {"value": passes * sample_flops / ct / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "sample": f"{passes} passes over {idx.size} rows (the first 8 of each expert), {ct:.1f} s"}
+
+    line = {
+        "metric": METRICS["grouped"] + f" ({w.name}{', y only' if args.no_x else ''})",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": "grouped", "tokens": w.tokens, "hidden": w.hidden, "inter": w.inter,
+                   "experts": w.experts, "limit": w.limit, "write_x": not args.no_x,
+                   "io": "bf16 a / weights / y / x, fp32 probs; bf16 MFMA products, fp32 accumulation",
+                   "flops_per_step": flops},
+        "frac_of_peak": value / PEAK_BF16_TFLOPS,
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -157,6 +157,46 @@ int router_weight_mul_bwd_typed(const void *grad_out, int grad_out_dtype, const 
                                 const float *probs, void *grad_x, float *grad_probs, int64_t rows,
                                 int64_t hidden, void *stream);
 
+/*
+ * gate_up grouped GEMM with the clamped SwiGLU x probability epilogue fused
+ * into it (the step before the epilogue above, done in one kernel).
+ * Defined by three pages:
+ *   "nemo_automodel.components.moe.mok_experts": the routed gate and up
+ *     weights are contiguous bf16 [local_experts, expert_intermediate, hidden];
+ *   "nemo_automodel.components.moe.quantized_experts",
+ *     MXFP4ExpertStorageMixin._mxfp4_base_mm: the routed activations are
+ *     [tokens, in_dim] grouped contiguously by local expert, offs is an int32
+ *     [local_experts] tensor of cumulative token counts, and the product is
+ *     [tokens, out_dim] in the activation dtype;
+ *   "nemo_automodel.components.moe.swiglu_triton": the epilogue on that output.
+ * Rows of expert e are [start_e, end_e): start_0 = 0, end_e = offs[e]
+ * clamped to [start_e, tokens], start_{e+1} = end_e. For such a row t:
+ *   gate[t, j] = bf16( sum_h a[t, h] * w_gate[e, j, h] )   (float32 accumulation)
+ *   up[t, j]   = bf16( sum_h a[t, h] * w_up[e, j, h] )
+ *   y[t, j]    = bf16( silu(min(gate, L)) * clamp(up, -L, L) * probs[t] )
+ * i.e. swiglu_clamped_fwd of x = [gate | up]. Rows at or past the last end
+ * belong to no expert: neither y nor x_out is written there.
+ *   a       [tokens, hidden] bf16                  in, rows grouped by expert
+ *   w_gate  [experts, inter, hidden] bf16          in
+ *   w_up    [experts, inter, hidden] bf16          in
+ *   offs    [experts] int32, device memory         in (read on the device only)
+ *   probs   [tokens] float32                       in
+ *   y       [tokens, inter] bf16                   out
+ *   x_out   [tokens, 2*inter] bf16                 out, may be NULL: [gate | up] as
+ *                                                  swiglu_clamped_bwd takes it
+ *   limit   L, finite and > 0
+ * hidden and inter must be multiples of 8 (MOE_EPI_ERR_BAD_SHAPE otherwise;
+ * there is no per-element path), tokens at most INT32_MAX (offs is int32);
+ * a, w_gate, w_up, y and x_out 16-byte aligned, offs and probs 4-byte
+ * aligned (MOE_EPI_ERR_MISALIGNED). Outputs may not overlap any input or each
+ * other (MOE_EPI_ERR_ALIAS). The caller owns every buffer; the library
+ * allocates nothing and queues the work on `stream`. Returns a moe_epi_status.
+ */
+int grouped_gate_up_swiglu_fwd(const uint16_t *a, const uint16_t *w_gate, const uint16_t *w_up,
+                               const int32_t *offs, const float *probs, uint16_t *y, uint16_t *x_out,
+                               int64_t tokens, int64_t hidden, int64_t inter, int64_t experts, float limit,
+                               void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *moe_epi_status_string(int status);
 

@@ -67,9 +67,10 @@ def lib() -> ctypes.CDLL:
     L.swiglu_clamped_bwd_typed.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp]
     L.router_weight_mul_fwd_typed.argtypes = [vp, i32, vp, vp, i32, i64, i64, vp]
     L.router_weight_mul_bwd_typed.argtypes = [vp, i32, vp, i32, vp, vp, vp, i64, i64, vp]
+    L.grouped_gate_up_swiglu_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp]
     for name in ("swiglu_clamped_fwd", "swiglu_clamped_bwd", "router_weight_mul_fwd", "router_weight_mul_bwd",
                  "swiglu_clamped_fwd_typed", "swiglu_clamped_bwd_typed", "router_weight_mul_fwd_typed",
-                 "router_weight_mul_bwd_typed"):
+                 "router_weight_mul_bwd_typed", "grouped_gate_up_swiglu_fwd"):
         getattr(L, name).restype = ctypes.c_int
     L.moe_epi_status_string.argtypes = [ctypes.c_int]
     L.moe_epi_status_string.restype = ctypes.c_char_p
@@ -204,6 +205,31 @@ def router_weight_mul_bwd(grad_out, x, probs, grad_x, grad_probs, stream=None) -
         status = lib().router_weight_mul_bwd_typed(_ptr(grad_out), oc, xp, xc, _ptr(probs), _ptr(grad_x),
                                                    _ptr(grad_probs), rows, hidden, st)
     _check(status, "router_weight_mul_bwd")
+
+
+def grouped_gate_up_swiglu_fwd(a, w_gate, w_up, offs, probs, y, x_out, limit: float, stream=None) -> None:
+    """Fused gate_up grouped GEMM + clamped SwiGLU x probs. a [tokens, hidden] bf16 (rows grouped by
+    expert); w_gate, w_up [experts, inter, hidden] bf16; offs int32 [experts] cumulative token counts
+    (on the device); probs fp32 [tokens] or [tokens, 1]; y [tokens, inter] bf16; x_out None or
+    [tokens, 2*inter] bf16 (gate | up, the backward's input)."""
+    tokens, hidden = _rows_cols(a, "a")
+    if w_gate.dim() != 3:
+        raise ValueError(f"w_gate must be 3-D [experts, inter, hidden], got {tuple(w_gate.shape)}")
+    experts, inter = int(w_gate.shape[0]), int(w_gate.shape[1])
+    dev = a.device
+    _need(a, "a", torch.bfloat16, [(tokens, hidden)], dev)
+    _need(w_gate, "w_gate", torch.bfloat16, [(experts, inter, hidden)], dev)
+    _need(w_up, "w_up", torch.bfloat16, [(experts, inter, hidden)], dev)
+    _need(offs, "offs", torch.int32, [(experts,)], dev)
+    _need(probs, "probs", torch.float32, [(tokens,), (tokens, 1)], dev)
+    _need(y, "y", torch.bfloat16, [(tokens, inter)], dev)
+    if x_out is not None:
+        _need(x_out, "x_out", torch.bfloat16, [(tokens, 2 * inter)], dev)
+    st = _stream_handle(a, stream)
+    status = lib().grouped_gate_up_swiglu_fwd(a.data_ptr(), w_gate.data_ptr(), w_up.data_ptr(), offs.data_ptr(),
+                                              probs.data_ptr(), y.data_ptr(), _ptr(x_out), tokens, hidden, inter,
+                                              experts, float(limit), st)
+    _check(status, "grouped_gate_up_swiglu_fwd")
 
 
 # ---- allocating helpers and autograd wrappers ------------------------------

@@ -30,6 +30,7 @@
 //     fp32 multiplies in the order of the defining expression (built with
 //     -ffp-contract=off).
 #include "epi_common.h"
+#include "swiglu_math.h"
 
 namespace moe_epi {
 namespace {
@@ -37,27 +38,6 @@ namespace {
 // block sizes of the per-element kernels
 constexpr int kFwdBlock = 256;
 constexpr int kBwdBlock = 128;
-
-// sigma(z) = 1 / (1 + e^-z) with e^-z = 2^(-z * log2(e)).
-__device__ __forceinline__ float sigmoid_f32(float z) {
-    const float e = __builtin_amdgcn_exp2f(z * -1.4426950408889634f);
-    return __builtin_amdgcn_rcpf(1.0f + e);
-}
-
-// clamp(gate, max=L): a comparison with NaN is false, so NaN passes through.
-__device__ __forceinline__ float clamp_hi(float g, float L) { return (g > L) ? L : g; }
-
-// clamp(up, -L, L), NaN passes through.
-__device__ __forceinline__ float clamp_sym(float u, float L) {
-    return (fabsf(u) > L) ? copysignf(L, u) : u;
-}
-
-__device__ __forceinline__ float fwd_elem(float g, float u, float p, float L) {
-    const float gc = clamp_hi(g, L);
-    const float uc = clamp_sym(u, L);
-    const float s = sigmoid_f32(gc);
-    return ((gc * s) * uc) * p;
-}
 
 // d_gate, d_up for one element; adds this element's probability-gradient term
 // gy * silu(gc) * uc to acc when kGradProbs.

@@ -1,0 +1,37 @@
+// Element math of the clamped SwiGLU forward, shared by the streaming kernels
+// and the grouped-GEMM epilogue so that both compute the same bits.
+//
+// Operation (page "nemo_automodel.components.moe.swiglu_triton", module
+// description): y = silu(min(gate, L)) * clamp(up, -L, L) * p in fp32, the
+// product taken left to right. Clamps are compare/select, so NaN passes
+// through as in torch.clamp; exp is v_exp_f32 of -z * log2(e) and 1/(1+e) is
+// v_rcp_f32; the rest are fp32 multiplies (the library is built with
+// -ffp-contract=off, so none is fused).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace moe_epi {
+
+// sigma(z) = 1 / (1 + e^-z) with e^-z = 2^(-z * log2(e)).
+__device__ __forceinline__ float sigmoid_f32(float z) {
+    const float e = __builtin_amdgcn_exp2f(z * -1.4426950408889634f);
+    return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// clamp(gate, max=L): a comparison with NaN is false, so NaN passes through.
+__device__ __forceinline__ float clamp_hi(float g, float L) { return (g > L) ? L : g; }
+
+// clamp(up, -L, L), NaN passes through.
+__device__ __forceinline__ float clamp_sym(float u, float L) {
+    return (fabsf(u) > L) ? copysignf(L, u) : u;
+}
+
+__device__ __forceinline__ float fwd_elem(float g, float u, float p, float L) {
+    const float gc = clamp_hi(g, L);
+    const float uc = clamp_sym(u, L);
+    const float s = sigmoid_f32(gc);
+    return ((gc * s) * uc) * p;
+}
+
+}  // namespace moe_epi

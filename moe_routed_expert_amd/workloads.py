@@ -183,6 +183,107 @@ WORKLOADS = {
 HEADLINE = "swiglu_131072x2048"
 
 
+# ---- gate_up grouped GEMM + epilogue ------------------------------------------
+#
+# Inputs of the fused grouped GEMM (pages: nemo_automodel.components.moe
+# .mok_experts for the weight layout [local_experts, expert_intermediate,
+# hidden]; .quantized_experts, _mxfp4_base_mm, for tokens grouped by expert with
+# cumulative int32 counts offs). Readings taken where the pages give no numbers:
+#   - tokens are split over the local experts by a multinomial draw with
+#     Dirichlet(2, ..., 2) proportions (uneven, as routing is); "one_empty"
+#     forces one expert to receive no token, "even" splits evenly;
+#   - a ~ N(0, a_sigma^2) and each weight ~ N(0, (gate_up_sigma / (a_sigma *
+#     sqrt(hidden)))^2), so that gate and up come out ~ N(0, gate_up_sigma^2):
+#     with gate_up_sigma = 4 that is the x ~ N(0, 4^2) of the epilogue's
+#     131072 x 2048 workload, and the clamps at L = 10 engage as they do there;
+#   - hidden = 7168 is the router workload's width, and 8 local experts per GPU
+#     is a reading (the pages give no local expert count);
+#   - probs ~ U(0, 1) fp32.
+# Draws use their own SeedSequence streams (kinds 10-14), chunked like the rest.
+
+@dataclass(frozen=True)
+class GroupedWorkload:
+    name: str
+    tokens: int
+    hidden: int
+    inter: int
+    experts: int
+    limit: float
+    seed: int
+    a_sigma: float = 1.0
+    gate_up_sigma: float = 4.0
+    split: str = "dirichlet"      # "dirichlet" | "one_empty" | "even"
+
+    def flops(self) -> int:
+        """Multiply-adds of the two products, counted as 2 flops each."""
+        return 2 * self.tokens * self.hidden * 2 * self.inter
+
+    def min_bytes(self, write_x: bool = True) -> int:
+        """Algorithmic HBM bytes: a, both weight tensors, probs and offs read once,
+        y (and x = [gate | up]) written once."""
+        t, h, i, e = self.tokens, self.hidden, self.inter, self.experts
+        return t * h * 2 + 2 * e * i * h * 2 + 4 * t + 4 * e + t * i * 2 + (t * 2 * i * 2 if write_x else 0)
+
+    def counts(self) -> np.ndarray:
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(self.seed, spawn_key=(10, 0))))
+        e = self.experts
+        if self.split == "even":
+            c = np.full(e, self.tokens // e, dtype=np.int64)
+            c[: self.tokens % e] += 1
+            return c
+        if self.split == "one_empty" and e > 1:
+            c = g.multinomial(self.tokens, g.dirichlet(np.full(e - 1, 2.0)))
+            return np.insert(c, e // 2, 0)
+        if self.split not in ("dirichlet", "one_empty"):
+            raise ValueError(self.split)
+        return g.multinomial(self.tokens, g.dirichlet(np.full(e, 2.0)))
+
+    def offs(self) -> np.ndarray:
+        return np.cumsum(self.counts()).astype(np.int32)
+
+    def generate(self, threads: int | None = None) -> dict:
+        """a [tokens, hidden], w_gate / w_up [experts, inter, hidden] (bf16 bits as
+        uint16), offs int32 [experts], probs float32 [tokens]."""
+        t, h, i, e = self.tokens, self.hidden, self.inter, self.experts
+        w_sigma = np.float32(self.gate_up_sigma / (self.a_sigma * np.sqrt(h)))
+        a = np.empty((t, h), dtype=np.uint16)
+        w_gate = np.empty((e, i, h), dtype=np.uint16)
+        w_up = np.empty((e, i, h), dtype=np.uint16)
+
+        def rng(kind: int, chunk: int) -> np.random.Generator:
+            return np.random.Generator(np.random.PCG64(np.random.SeedSequence(self.seed, spawn_key=(kind, chunk))))
+
+        def fill_a(chunk: int) -> None:
+            r0 = chunk * CHUNK_ROWS
+            m = min(CHUNK_ROWS, t - r0)
+            f = rng(11, chunk).standard_normal((m, h), dtype=np.float32)
+            f *= np.float32(self.a_sigma)
+            a[r0:r0 + m] = _to_bf16_bits(f)
+
+        def fill_w(job: tuple) -> None:
+            which, ex = job
+            f = rng(12 + which, ex).standard_normal((i, h), dtype=np.float32)
+            f *= w_sigma
+            (w_gate if which == 0 else w_up)[ex] = _to_bf16_bits(f)
+
+        jobs_a = range((t + CHUNK_ROWS - 1) // CHUNK_ROWS)
+        jobs_w = [(which, ex) for which in (0, 1) for ex in range(e)]
+        workers = threads or max(1, min(16, os.cpu_count() or 1))
+        with ThreadPoolExecutor(workers) as pool:
+            list(pool.map(fill_a, jobs_a))
+            list(pool.map(fill_w, jobs_w))
+        probs = rng(14, 0).random(t, dtype=np.float32)
+        return {"a": a, "w_gate": w_gate, "w_up": w_up, "offs": self.offs(), "probs": probs}
+
+
+GROUPED_WORKLOADS = {
+    w.name: w for w in [
+        GroupedWorkload("grouped_4096x1024x512_e5", 4096, 1024, 512, 5, 10.0, seed=20, split="one_empty"),
+        GroupedWorkload("grouped_131072x7168x2048_e8", 131072, 7168, 2048, 8, 10.0, seed=21),
+    ]
+}
+
+
 def custom(op: str, rows: int, cols: int, limit: float | None = None, x_sigma: float = 4.0,
            seed: int = 0, **kw) -> Workload:
     """An ad-hoc workload (test shapes: ragged tails, tiny rows, odd widths)."""

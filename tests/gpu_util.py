@@ -117,3 +117,33 @@ def assert_f32_within(got: np.ndarray, want: np.ndarray, bound: np.ndarray, what
     bad = err > bound[ok]
     assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond the float32 bound"
     return {"max_err_over_bound": float((err / bound[ok]).max(initial=0)), "exact": float((err == 0).mean())}
+
+
+# ---- grouped GEMM output (bf16 of an fp32-accumulated sum) ---------------------
+#
+# The kernel accumulates the K = hidden exact bf16 products in fp32 (in the MFMA
+# units' order) and rounds the sum once to bf16. Against the exact sum S, an fp32
+# accumulation of K terms in any order errs by at most gamma_K * sum|a*w| with
+# gamma_K = K u / (1 - K u), u = 2^-24; the bar doubles that (an accumulator that
+# truncated instead of rounding would still pass) and adds half a bf16 ulp for
+# the final rounding.
+
+def bf16_spacing(v: np.ndarray) -> np.ndarray:
+    """bfloat16 ulp at |v| (subnormal spacing 2^-133 below 2^-126)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def assert_gemm_bf16_within(got_bits: np.ndarray, exact: np.ndarray, abs_sum: np.ndarray, k: int, what: str) -> dict:
+    from tests.numerics import bf16_bits_to_f32
+    got = bf16_bits_to_f32(got_bits).astype(np.float64)
+    u = 2.0 ** -24
+    gamma = k * u / (1 - k * u)
+    bound = 2 * gamma * abs_sum + 0.5 * bf16_spacing(np.maximum(np.abs(got), np.abs(exact)))
+    err = np.abs(got - exact)
+    bad = ~(err <= bound)
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {got.size} beyond the fp32-accumulation bound"
+    from tests.numerics import f64_to_bf16_exact
+    return {"n": int(got.size), "equal_to_exact_rounding": float((got_bits == f64_to_bf16_exact(exact)).mean()),
+            "max_err_over_bound": float((err / bound).max(initial=0))}

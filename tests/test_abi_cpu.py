@@ -159,3 +159,44 @@ def test_binding_rejects_cpu_tensors_before_the_library():
         binding.swiglu_clamped_fwd(x.double(), p, y, 7.0)
     with pytest.raises(ValueError):
         binding.router_weight_mul_fwd(x[:, :7], p, y[:, :7])
+
+
+# ---- grouped gate_up GEMM + epilogue ------------------------------------------
+
+F = 0x60_0000_0000
+G = 0x70_0000_0000
+
+
+def gr(L, a=A, wg=B, wu=C, offs=D, p=E, y=F, x=G, tokens=256, hidden=64, inter=32, experts=4, lim=7.0):
+    return L.grouped_gate_up_swiglu_fwd(a, wg, wu, offs, p, y, x, tokens, hidden, inter, experts, lim, None)
+
+
+def test_grouped_validation(L):
+    for kw in ({"a": None}, {"wg": None}, {"wu": None}, {"offs": None}, {"p": None}, {"y": None}):
+        assert gr(L, **kw) == NULLP, kw
+    for kw in ({"tokens": -1}, {"hidden": 0}, {"inter": 0}, {"experts": 0}, {"hidden": 60}, {"inter": 36},
+               {"tokens": 2 ** 31}, {"experts": 2 ** 62, "inter": 8}):
+        assert gr(L, **kw) == SHAPE, kw
+    for lim in (0.0, -1.0, float("inf"), float("nan")):
+        assert gr(L, lim=lim) == LIMIT
+    assert gr(L, tokens=0) == OK                       # nothing to do, nothing launched
+    assert gr(L, tokens=0, a=None) == OK               # pointers are not needed for an empty call
+    for kw in ({"a": A + 2}, {"wg": B + 8}, {"wu": C + 4}, {"y": F + 2}, {"x": G + 8}, {"offs": D + 2},
+               {"p": E + 1}):
+        assert gr(L, **kw) == MISAL, kw
+    assert gr(L, y=A) == ALIAS                         # y on top of a
+    assert gr(L, x=B) == ALIAS                         # x_out on top of w_gate
+    assert gr(L, x=F + 16) == ALIAS                    # x_out overlapping y
+    assert gr(L, y=D) == ALIAS                         # y on top of offs
+
+
+def test_grouped_binding_rejects_bad_tensors():
+    a = torch.zeros(16, 64, dtype=torch.bfloat16)
+    w = torch.zeros(2, 32, 64, dtype=torch.bfloat16)
+    offs = torch.tensor([8, 16], dtype=torch.int32)
+    p = torch.zeros(16)
+    y = torch.zeros(16, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):                    # CPU tensors
+        binding.grouped_gate_up_swiglu_fwd(a, w, w, offs, p, y, None, 7.0)
+    with pytest.raises(ValueError):                    # 2-D weights
+        binding.grouped_gate_up_swiglu_fwd(a, w[0], w[0], offs, p, y, None, 7.0)

@@ -1,0 +1,134 @@
+"""GPU parity of the fused gate_up grouped GEMM + clamped SwiGLU epilogue
+(grouped_gate_up_swiglu_fwd) against the oracle.
+
+Two separate bars (tests/gpu_util.py):
+  - x = [gate | up], the grouped-GEMM output in bf16, against the oracle's exact
+    sums: within the bound of an fp32 accumulation of `hidden` products plus half
+    a bf16 ulp;
+  - y against the oracle's clamped SwiGLU forward of the kernel's own x: the
+    streaming forward's bar (1 bf16 ulp, zeros bit-exact), since the epilogue
+    computes from the bf16 gate and up.
+The call without x_out must give bit-identical y, and rows of no expert must be
+left untouched.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_routed_expert_amd as epi
+import oracle
+from moe_routed_expert_amd.workloads import GROUPED_WORKLOADS, GroupedWorkload
+from tests.gpu_util import assert_bf16_parity, assert_gemm_bf16_within, to_dev_bf16, to_host_bits
+
+pytestmark = pytest.mark.gpu
+SENTINEL = 0x7FBF   # a NaN pattern the kernel never writes
+
+
+def say(msg):
+    print(f"\n[gpu-grouped] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    epi.binding.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def run(d, tokens, hidden, inter, experts, L, with_x=True):
+    a, wg, wu = to_dev_bf16(d["a"]), to_dev_bf16(d["w_gate"]), to_dev_bf16(d["w_up"])
+    offs = torch.from_numpy(d["offs"]).cuda()
+    p = torch.from_numpy(d["probs"]).cuda()
+    y = torch.full((tokens, inter), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    x = torch.full((tokens, 2 * inter), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16) \
+        if with_x else None
+    epi.grouped_gate_up_swiglu_fwd(a, wg, wu, offs, p, y, x, L)
+    torch.cuda.synchronize()
+    return to_host_bits(y), (to_host_bits(x) if with_x else None)
+
+
+def covered_rows(offs, tokens):
+    cov = np.zeros(tokens, bool)
+    start = 0
+    for c in offs:
+        end = min(max(int(c), start), tokens)
+        cov[start:end] = True
+        start = end
+    return cov
+
+
+def check(d, tokens, hidden, inter, experts, L, what):
+    y, x = run(d, tokens, hidden, inter, experts, L)
+    cov = covered_rows(d["offs"], tokens)
+    assert (y[~cov] == SENTINEL).all() and (x[~cov] == SENTINEL).all(), f"{what}: rows of no expert written"
+    s, s_abs = oracle.grouped_gate_up(d["a"], d["w_gate"], d["w_up"], d["offs"], tokens, hidden, inter, experts,
+                                      with_abs_sum=True)
+    sx = assert_gemm_bf16_within(x[cov], s[cov], s_abs[cov], hidden, f"{what} x")
+    y_o = oracle.swiglu_clamped_fwd(x[cov], d["probs"][cov], int(cov.sum()), inter, L)
+    sy = assert_bf16_parity(y[cov], y_o, f"{what} y")
+    y2, _ = run(d, tokens, hidden, inter, experts, L, with_x=False)
+    assert np.array_equal(y2, y), f"{what}: y differs without x_out"
+    say(f"{what}: x {sx}, y exact {sy['exact']:.5f}")
+
+
+def test_small_named_workload():
+    w = GROUPED_WORKLOADS["grouped_4096x1024x512_e5"]
+    check(w.generate(), w.tokens, w.hidden, w.inter, w.experts, w.limit, w.name)
+
+
+# tails in every dimension: tokens not a multiple of 128 per expert, hidden not a
+# multiple of 32 (a partial K step), inter not a multiple of 128 (a partial column
+# tile), a single expert, many small experts, an empty expert
+@pytest.mark.parametrize("tokens,hidden,inter,experts,split", [
+    (300, 64, 128, 3, "dirichlet"), (257, 200, 136, 4, "one_empty"), (1000, 512, 256, 1, "even"),
+    (129, 96, 8, 7, "dirichlet"), (640, 1032, 264, 16, "dirichlet"), (1, 8, 8, 1, "even"),
+])
+def test_shapes(tokens, hidden, inter, experts, split):
+    w = GroupedWorkload(f"g_{tokens}x{hidden}x{inter}_e{experts}", tokens, hidden, inter, experts, 7.0,
+                        seed=tokens + hidden + inter + experts, split=split, gate_up_sigma=5.0)
+    check(w.generate(), tokens, hidden, inter, experts, w.limit, w.name)
+
+
+@pytest.mark.parametrize("offs", [[50, 20, 300, 100], [0, 0, 0, 257], [257, 257, 257, 257], [-5, 10, 10, 200],
+                                  [100, 1000, 5, 7]])
+def test_counts_that_are_empty_decreasing_or_too_large(offs):
+    w = GroupedWorkload("g_offs", 257, 64, 32, 4, 7.0, seed=31)
+    d = w.generate()
+    d["offs"] = np.array(offs, dtype=np.int32)
+    check(d, 257, 64, 32, 4, 7.0, f"offs {offs}")
+
+
+def test_full_size_sampled_rows():
+    w = GROUPED_WORKLOADS["grouped_131072x7168x2048_e8"]
+    say(f"{w.name}: generate")
+    d = w.generate()
+    say(f"{w.name}: gpu (with and without x)")
+    y, x = run(d, w.tokens, w.hidden, w.inter, w.experts, w.limit)
+    y2, _ = run(d, w.tokens, w.hidden, w.inter, w.experts, w.limit, with_x=False)
+    assert np.array_equal(y, y2)
+    assert not (y == SENTINEL).any()
+    # sampled rows: each expert's first and last rows, rows at 128-row tile edges, random rows
+    offs = d["offs"].astype(np.int64)
+    starts = np.concatenate([[0], offs[:-1]])
+    rng = np.random.default_rng(5)
+    pick = set()
+    for s0, e0 in zip(starts, offs):
+        if e0 > s0:
+            pick |= {s0, s0 + 1, e0 - 1, min(s0 + 127, e0 - 1), min(s0 + 128, e0 - 1)}
+    pick |= set(rng.integers(0, w.tokens, 200).tolist())
+    idx = np.array(sorted(pick))
+    # the oracle on the sampled rows: regroup them by expert with their own offs
+    expert_of = np.searchsorted(offs, idx, side="right")
+    sub_offs = np.array([np.sum(expert_of <= e) for e in range(w.experts)], dtype=np.int32)
+    say(f"{w.name}: oracle on {idx.size} sampled rows")
+    s, s_abs = oracle.grouped_gate_up(d["a"][idx], d["w_gate"], d["w_up"], sub_offs, idx.size, w.hidden, w.inter,
+                                      w.experts, with_abs_sum=True)
+    sx = assert_gemm_bf16_within(x[idx], s, s_abs, w.hidden, f"{w.name} x")
+    y_o = oracle.swiglu_clamped_fwd(x[idx], d["probs"][idx], idx.size, w.inter, w.limit)
+    sy = assert_bf16_parity(y[idx], y_o, f"{w.name} y")
+    say(f"{w.name}: x {sx}, y exact {sy['exact']:.5f}")
