@@ -76,15 +76,25 @@ def parse_args():
     return ap.parse_args()
 
 
-def kernel_source_digest() -> str:
-    """Digest of the HIP sources and build flags, to tell whether counter
-    readings taken earlier still describe the kernels being timed."""
+# The sources each op's kernels are built from (with the public header and
+# the build flags): a counter record stays valid while these are unchanged.
+KERNEL_SOURCES = {
+    "swiglu": ("swiglu_clamped.hip", "swiglu_math.h", "epi_common.h"),
+    "router": ("router_weight_mul.hip", "epi_common.h"),
+    "grouped": ("grouped_swiglu.hip", "swiglu_math.h", "epi_common.h"),
+}
+
+
+def kernel_source_digest(op: str) -> str:
+    """Digest of one op's HIP sources and the build flags, to tell whether
+    counter readings taken earlier still describe the kernels being timed."""
     from moe_routed_expert_amd import build as hip_build
     h = hashlib.sha256()
-    for path in hip_build.sources() + [os.path.join(hip_build.CSRC, "epi_common.h"),
-                                       os.path.join(ROOT, "include", "moe_epi.h")]:
-        with open(path, "rb") as fh:
+    for name in KERNEL_SOURCES[op]:
+        with open(os.path.join(hip_build.CSRC, name), "rb") as fh:
             h.update(fh.read())
+    with open(os.path.join(ROOT, "include", "moe_epi.h"), "rb") as fh:
+        h.update(fh.read())
     h.update(" ".join(hip_build.FLAGS).encode())
     return h.hexdigest()[:16]
 
@@ -113,7 +123,8 @@ def load_traffic(kernel: str, workload) -> float | None:
         return None
     block = text[start + len("```json"):text.find("```", start + 7)]
     rec = json.loads(block)
-    if rec.get("kernel_source_digest") != kernel_source_digest():
+    op = "grouped" if hasattr(workload, "experts") else workload.op
+    if rec.get("kernel_source_digest") != kernel_source_digest(op):
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")

@@ -25,24 +25,34 @@
 //     tile of up (so each output's gate and up sit in the same lane), with
 //     eight wavefronts (4 x 2) of 64 x 64 each: 2 x 2 v_mfma_f32_32x32x16_bf16
 //     tiles for gate and 2 x 2 for up, 128 fp32 accumulators per lane, two
-//     wavefronts per SIMD.
-//   * K advances 64 at a time through double-buffered LDS tiles of A, W_gate
-//     and W_up (rows padded by 16 bytes, which makes the 16-byte fragment
-//     reads conflict-free; 144 KiB in all, one block per CU); the next K
-//     step's global loads are in flight while the current one's MFMAs run.
-//     One barrier per K step. Of 14 tile shapes measured at 131072 x 7168 x
-//     2048 (64-256 tokens, 64-256 columns, K steps of 32 and 64, 1-3 waves per
-//     SIMD; every shape gives bit-identical results, since each output is
-//     accumulated in the same order), this one ran fastest.
+//     wavefronts per SIMD, one block per CU (128 KiB of LDS).
+//   * Operands go from global memory straight into LDS (global_load_lds_dwordx4),
+//     K steps of 64, two LDS stages: the next step's loads are in flight while
+//     this step's MFMAs run, with no registers spent on staging. Tiles are not
+//     padded (a wavefront's load fills 1 KiB contiguously); an XOR swizzle of
+//     each row's 16-byte chunks keeps the fragment reads conflict-free.
+//   * Within a K step, the next 16-wide sub-step's fragments are read from LDS
+//     while the current one's MFMAs run. One barrier per K step, a bare
+//     s_barrier after explicit waits (a __syncthreads() fence would also wait
+//     for the loads still in flight).
 //   * Tiles never straddle experts: each block finds its expert and row range
 //     from offs on the device (no host copy of offs), so a grid sized for
 //     the worst case, ceil(tokens / 256) + experts row tiles, covers any split.
 //   * XCD-aware order: consecutive block ids land on different XCDs, so the
 //     block id is remapped to give each XCD a contiguous range of tiles, and
-//     the column tiles that share one A tile run on the same XCD (and L2).
+//     those are visited in groups of 4 row tiles, so that the blocks running
+//     together on one XCD share both their A tiles and their weight tiles in
+//     that XCD's L2.
 //   * Epilogue: accumulators are rounded to bf16, the SwiGLU is applied, and
 //     each output tile is staged through LDS so that global stores are
 //     16-byte, row-contiguous accesses.
+// Measured at 131072 x 7168 x 2048 with 8 experts (every configuration gives
+// bit-identical results, each output being accumulated in the same order):
+// register-staged loads with padded LDS ran at 746-918 TFLOP/s over 22 tile
+// shapes, deeper load pipelines and fragment pipelining at up to 953, and this
+// configuration at 965 (988 without x_out). Hardware counters put LDS bank
+// conflicts at 0.5% of LDS cycles and show the wavefronts waiting about half
+// their cycles (loads and barriers of a single resident block).
 #include "epi_common.h"
 #include "swiglu_math.h"
 
@@ -53,34 +63,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kXcds = 8;  // MI355X: 8 XCDs, work-groups dispatched round-robin over them
-
-// Tile configuration: a block computes BM tokens x BN columns of gate and the
-// same columns of up, with WM x WN wavefronts (each BM/WM x BN/WN of both),
-// stepping BK along hidden; OCC wavefronts per SIMD is the occupancy the
-// compiler must leave room for (it caps the registers per lane at 512 / OCC).
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int OCC_>
-struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, OCC = OCC_;
-    static constexpr int kThreads = 64 * WM * WN;
-    static constexpr int MI = BM / (32 * WM);        // 32 x 32 MFMA tiles per wavefront, along tokens
-    static constexpr int NI = BN / (32 * WN);        // ... along columns (for gate, and again for up)
-    static constexpr int kLdk = BK + 8;              // LDS row stride of a K tile, in bf16 (16 bytes of padding)
-    static constexpr int kAElems = BM * kLdk;
-    static constexpr int kWElems = BN * kLdk;
-    static constexpr int kStageElems = kAElems + 2 * kWElems;
-    static constexpr int kLdo = BN + 8;              // LDS row stride of a staged output tile, in bf16
-    static constexpr int kAChunks = BM * BK / 8 / kThreads;  // 16-byte chunks per thread per K step
-    static constexpr int kWChunks = BN * BK / 8 / kThreads;
-    static_assert(MI >= 1 && NI >= 1 && BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "whole MFMA tiles");
-    static_assert(BK % 16 == 0 && kAChunks >= 1 && kWChunks >= 1 && BM * BK % (8 * kThreads) == 0 &&
-                  BN * BK % (8 * kThreads) == 0, "whole 16-byte chunks per thread");
-    // LDS holds two K-step buffers, then (after the K loop) one staged output tile
-    static constexpr int kLdsElems = 2 * kStageElems > BM * kLdo ? 2 * kStageElems : BM * kLdo;
-    static_assert(BM * BN % (8 * kThreads) == 0, "whole output chunks per thread");
-};
-
-// The configuration the library launches (see the shape notes above).
-using Prod = Cfg<256, 128, 64, 4, 2, 2>;
 
 struct TileRows {
     int64_t row0;   // first token of the tile
@@ -108,37 +90,20 @@ __device__ TileRows find_row_tile(const int32_t* __restrict__ offs, int64_t toke
     return TileRows{0, 0, 0};
 }
 
-// Global -> registers: this thread's 16-byte chunks of an operand tile of
-// `rows_tile` rows (rows [0, nrows) valid; columns k0 + [0, BK) of a
-// row-major matrix with `ld` elements per row, those at or past kend zero).
-template <class C, int N>
-__device__ __forceinline__ void load_chunks(u32x4 (&r)[N], const uint16_t* __restrict__ base, int64_t ld, int nrows,
-                                            int64_t k0, int64_t kend) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const int c = static_cast<int>(threadIdx.x) + i * C::kThreads;
-        const int row = c / (C::BK / 8), kq = c % (C::BK / 8);
-        const int64_t k = k0 + kq * 8;
-        if (row < nrows && k < kend)
-            r[i] = *reinterpret_cast<const u32x4*>(base + row * ld + k);
-        else
-            r[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-}
-
-template <class C, int N>
-__device__ __forceinline__ void store_chunks(uint16_t* tile, const u32x4 (&r)[N]) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const int c = static_cast<int>(threadIdx.x) + i * C::kThreads;
-        const int row = c / (C::BK / 8), kq = c % (C::BK / 8);
-        *reinterpret_cast<u32x4*>(tile + row * C::kLdk + kq * 8) = r[i];
-    }
-}
-
-template <class C>
-__device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int row, int k) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + row * C::kLdk + k));
+// Logical tile -> (row tile, column tile). Tiles are visited in groups of gm
+// row tiles: within a group the row tile changes fastest, so the blocks that
+// run together on one XCD (consecutive logical tiles) cover about gm row
+// tiles x (concurrent / gm) column tiles, and reuse both their A tiles and
+// their weight tiles from L2 instead of streaming one and re-reading the other.
+__device__ __forceinline__ void tile_of(int64_t logical, int64_t m_tiles, int64_t n_tiles, int gm, int64_t* mt,
+                                        int64_t* nt) {
+    const int64_t per_group = static_cast<int64_t>(gm) * n_tiles;
+    const int64_t group = logical / per_group;
+    const int64_t first = group * gm;
+    const int64_t rows_in_group = m_tiles - first < gm ? m_tiles - first : gm;
+    const int64_t in_group = logical % per_group;
+    *mt = first + in_group % rows_in_group;
+    *nt = in_group / rows_in_group;
 }
 
 __device__ __forceinline__ float round_bf16(float v) { return __uint_as_float(static_cast<uint32_t>(to_bf16(v)) << 16); }
@@ -172,6 +137,103 @@ __device__ __forceinline__ void store_tile(const uint16_t* stage, uint16_t* __re
     }
 }
 
+// Grid: row tiles (worst case ceil(tokens / BM) + experts) times column
+// tiles, rounded up to a multiple of the XCD count. Returns 0 when it does not
+// fit a 1-D grid.
+template <class C>
+int64_t grouped_grid(int64_t tokens, int64_t inter, int64_t experts, int64_t* n_tiles, int64_t* n_blocks) {
+    *n_tiles = (inter + C::BN - 1) / C::BN;
+    const int64_t m_bound = (tokens + C::BM - 1) / C::BM + experts;
+    *n_blocks = m_bound * *n_tiles;
+    const int64_t grid = (*n_blocks + kXcds - 1) / kXcds * kXcds;
+    return grid < (static_cast<int64_t>(1) << 31) ? grid : 0;
+}
+
+// ---- the kernel -------------------------------------------------------------------
+//
+// Global loads write straight into LDS (global_load_lds_dwordx4: each lane's
+// 16 bytes land at the wavefront's LDS base + 16 * lane), S - 1 K steps ahead
+// through a ring of S LDS stages, no register staging. A wavefront's load
+// fills 1 KiB of LDS contiguously, so tiles are not padded: chunk kq of a row
+// (BK / 8 chunks of 16 bytes) is placed at slot row * (BK / 8) + (kq ^ swz(row)),
+// which keeps the 16-byte fragment reads conflict-free. Chunks outside the
+// matrices (row or K tails) are written as zeros with an ordinary LDS store.
+template <int BM_, int BN_, int WM_, int WN_, int S_, int OCC_, int GM_ = 1, int BK_ = 32>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, S = S_, OCC = OCC_, GM = GM_;
+    static constexpr int kCpr = BK / 8;                // 16-byte chunks per row
+    static_assert(kCpr == 4 || kCpr == 8, "K steps of 32 or 64");
+    static constexpr int kThreads = 64 * WM * WN;
+    static constexpr int MI = BM / (32 * WM);
+    static constexpr int NI = BN / (32 * WN);
+    static constexpr int kAElems = BM * BK;            // no padding
+    static constexpr int kWElems = BN * BK;
+    static constexpr int kStageElems = kAElems + 2 * kWElems;
+    static constexpr int kLdo = BN + 8;
+    static constexpr int kAChunks = BM * BK / 8 / kThreads;
+    static constexpr int kWChunks = BN * BK / 8 / kThreads;
+    static constexpr int kDmaPerStage = kAChunks + 2 * kWChunks;  // load instructions per thread per stage
+    static constexpr int kLdsElems = S * kStageElems > BM * kLdo ? S * kStageElems : BM * kLdo;
+    static_assert(MI >= 1 && NI >= 1 && BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "whole MFMA tiles");
+    static_assert(kAChunks >= 1 && kWChunks >= 1 && BM * BK % (8 * kThreads) == 0 && BN * BK % (8 * kThreads) == 0,
+                  "whole 16-byte chunks per thread");
+    static_assert(S >= 2 && (S - 2) * kDmaPerStage <= 63, "outstanding loads fit the vmcnt counter");
+    static_assert(BM * BN % (8 * kThreads) == 0, "whole output chunks per thread");
+};
+
+// The configuration the library launches (see the kernel-shape notes at the top).
+using Prod = Cfg<256, 128, 4, 2, 2, 2, 4, 64>;
+
+// Swizzle of a row's chunks: any 8 consecutive rows, and any 16 consecutive
+// rows taken 4 or 8 apart, put the same chunk in different 16-byte bank groups.
+template <int kCpr>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (kCpr == 4)
+        return ((row >> 1) ^ (row >> 3)) & 3;
+    else
+        return (row ^ (row >> 3)) & 7;
+}
+
+// Slot (in 16-byte units) of chunk kq of row `row` in a swizzled tile.
+template <int kCpr>
+__device__ __forceinline__ int slot_of(int row, int kq) { return row * kCpr + (kq ^ swz<kCpr>(row)); }
+
+// Issue this thread's loads of one operand tile into `tile` (LDS): chunk i of
+// wavefront w covers slots [(i * threads + w * 64), +64), lane l slot + l.
+template <class C, int N>
+__device__ __forceinline__ void dma_tile(uint16_t* tile, const uint16_t* __restrict__ base, int64_t ld, int nrows,
+                                         int64_t k0, int64_t kend) {
+    const int lane = static_cast<int>(threadIdx.x) % 64;
+    const int wave = static_cast<int>(threadIdx.x) / 64;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int wave_slot0 = i * C::kThreads + wave * 64;  // uniform across the wavefront
+        const int slot = wave_slot0 + lane;
+        const int row = slot / C::kCpr;
+        const int kq = (slot % C::kCpr) ^ swz<C::kCpr>(row);
+        const int64_t k = k0 + kq * 8;
+        if (row < nrows && k < kend)
+            __builtin_amdgcn_global_load_lds(base + row * ld + k,
+                                             (__attribute__((address_space(3))) void*)(tile + wave_slot0 * 8), 16, 0,
+                                             0);
+        else
+            *reinterpret_cast<u32x4*>(tile + slot * 8) = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int kCpr>
+__device__ __forceinline__ bf16x8 frag_swz(const uint16_t* tile, int row, int kq) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + slot_of<kCpr>(row, kq) * 8));
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt in 6:4 left unconstrained, lgkmcnt in 11:8): this wavefront's loads
+// up to the last n issued have landed in LDS, and its own LDS stores are done.
+template <int N>
+__device__ __forceinline__ void wait_loads_but() {
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
 template <class C, bool kWriteX>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::OCC))) void grouped_gate_up_swiglu_kernel(
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ w_gate, const uint16_t* __restrict__ w_up,
@@ -179,15 +241,14 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     uint16_t* __restrict__ x_out, int64_t tokens, int64_t hidden, int64_t inter, int64_t experts, float L,
     int64_t n_tiles, int64_t n_blocks) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[C::kLdsElems];
-    constexpr int MI = C::MI, NI = C::NI;
+    constexpr int MI = C::MI, NI = C::NI, S = C::S;
 
-    // XCD-aware order: block b runs on XCD b % 8; XCD x takes logical tiles
-    // [x * per, (x + 1) * per). The grid is 8 * per blocks.
     const int64_t per = static_cast<int64_t>(gridDim.x) / kXcds;
     const int64_t logical = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
     if (logical >= n_blocks) return;
-    const int64_t mt = logical / n_tiles;
-    const int64_t col0 = (logical % n_tiles) * C::BN;
+    int64_t mt, nt;
+    tile_of(logical, n_blocks / n_tiles, n_tiles, C::GM, &mt, &nt);
+    const int64_t col0 = nt * C::BN;
     const TileRows tr = find_row_tile(offs, tokens, experts, mt, C::BM);
     if (tr.rows == 0) return;
     const int ncols = static_cast<int>(inter - col0 < C::BN ? inter - col0 : C::BN);
@@ -209,57 +270,74 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
             acc_u[mi][ni] = f32x16{};
         }
 
-    u32x4 ra[C::kAChunks], rg[C::kWChunks], ru[C::kWChunks];
     const int64_t nk = (hidden + C::BK - 1) / C::BK;
-    load_chunks<C>(ra, a_tile, hidden, tr.rows, 0, hidden);
-    load_chunks<C>(rg, g_tile, hidden, ncols, 0, hidden);
-    load_chunks<C>(ru, u_tile, hidden, ncols, 0, hidden);
-    store_chunks<C>(lds, ra);
-    store_chunks<C>(lds + C::kAElems, rg);
-    store_chunks<C>(lds + C::kAElems + C::kWElems, ru);
-    __syncthreads();
+    // Every wavefront issues exactly kDmaPerStage loads per stage only when no
+    // chunk of the tile lies outside the matrices (a wavefront whose chunk is
+    // out of range for all its lanes skips that load); otherwise the waits
+    // below fall back to waiting for every load.
+    const bool full = tr.rows == C::BM && ncols == C::BN && hidden % C::BK == 0;
+    auto issue = [&](int64_t kt) {
+        uint16_t* st = lds + (kt % S) * C::kStageElems;
+        const int64_t k0 = kt * C::BK;
+        dma_tile<C, C::kAChunks>(st, a_tile, hidden, tr.rows, k0, hidden);
+        dma_tile<C, C::kWChunks>(st + C::kAElems, g_tile, hidden, ncols, k0, hidden);
+        dma_tile<C, C::kWChunks>(st + C::kAElems + C::kWElems, u_tile, hidden, ncols, k0, hidden);
+    };
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+        if (s < nk) issue(s);
 
     for (int64_t kt = 0; kt < nk; ++kt) {
-        uint16_t* cur = lds + (kt & 1) * C::kStageElems;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            const int64_t k0 = (kt + 1) * C::BK;
-            load_chunks<C>(ra, a_tile, hidden, tr.rows, k0, hidden);
-            load_chunks<C>(rg, g_tile, hidden, ncols, k0, hidden);
-            load_chunks<C>(ru, u_tile, hidden, ncols, k0, hidden);
-        }
+        // this wavefront's loads of stage kt are done once at most the later
+        // stages' loads (kt + 1 .. kt + S - 2, those already issued) are pending
+        if (full && kt + S - 2 < nk)
+            wait_loads_but<(S - 2) * C::kDmaPerStage>();
+        else
+            wait_loads_but<0>();
+        // every wavefront's stage kt landed; stage kt - 1 is no longer read. A
+        // bare barrier: __syncthreads() would also wait for the later stages'
+        // loads still in flight (its fence covers every outstanding access).
+        // The empty asm statements keep the compiler from moving LDS accesses
+        // across the barrier (they emit no instruction).
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kt + S - 1 < nk) issue(kt + S - 1);
+        const uint16_t* cur = lds + (kt % S) * C::kStageElems;
         const uint16_t* sa = cur;
         const uint16_t* sg = cur + C::kAElems;
         const uint16_t* su = cur + C::kAElems + C::kWElems;
+        // the next 16-wide K sub-step's fragments are read while this one's
+        // MFMAs run (two register sets)
+        constexpr int KK = C::BK / 16;
+        bf16x8 fa[2][MI], fg[2][NI], fu[2][NI];
+        auto read = [&](int b, int kk) {
+            const int kq = kk * 2 + lane / 32;
 #pragma unroll
-        for (int kk = 0; kk < C::BK / 16; ++kk) {
-            const int k = kk * 16 + (lane / 32) * 8;
-            bf16x8 fa[MI], fg[NI], fu[NI];
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi) fa[mi] = frag<C>(sa, wm * (C::BM / C::WM) + mi * 32 + lane % 32, k);
+            for (int mi = 0; mi < MI; ++mi)
+                fa[b][mi] = frag_swz<C::kCpr>(sa, wm * (C::BM / C::WM) + mi * 32 + lane % 32, kq);
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni) {
-                fg[ni] = frag<C>(sg, wn * (C::BN / C::WN) + ni * 32 + lane % 32, k);
-                fu[ni] = frag<C>(su, wn * (C::BN / C::WN) + ni * 32 + lane % 32, k);
+                fg[b][ni] = frag_swz<C::kCpr>(sg, wn * (C::BN / C::WN) + ni * 32 + lane % 32, kq);
+                fu[b][ni] = frag_swz<C::kCpr>(su, wn * (C::BN / C::WN) + ni * 32 + lane % 32, kq);
             }
+        };
+        read(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            if (kk + 1 < KK) read((kk + 1) & 1, kk + 1);
+            const int b = kk & 1;
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni) {
-                    acc_g[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fg[ni], acc_g[mi][ni], 0, 0, 0);
-                    acc_u[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fu[ni], acc_u[mi][ni], 0, 0, 0);
+                    acc_g[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[b][mi], fg[b][ni], acc_g[mi][ni], 0, 0, 0);
+                    acc_u[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[b][mi], fu[b][ni], acc_u[mi][ni], 0, 0, 0);
                 }
         }
-        if (more) {
-            uint16_t* nxt = lds + ((kt + 1) & 1) * C::kStageElems;
-            store_chunks<C>(nxt, ra);
-            store_chunks<C>(nxt + C::kAElems, rg);
-            store_chunks<C>(nxt + C::kAElems + C::kWElems, ru);
-        }
-        __syncthreads();
     }
+    __syncthreads();  // all fragment reads done before the buffers become the staging tile
 
-    // ---- epilogue: y (and x) through an LDS staging tile -------------------
     uint16_t* stage = lds;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
@@ -302,34 +380,22 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     }
 }
 
-// Grid: row tiles (worst case ceil(tokens / BM) + experts) times column
-// tiles, rounded up to a multiple of the XCD count. Returns 0 when it does not
-// fit a 1-D grid.
-template <class C>
-int64_t grouped_grid(int64_t tokens, int64_t inter, int64_t experts, int64_t* n_tiles, int64_t* n_blocks) {
-    *n_tiles = (inter + C::BN - 1) / C::BN;
-    const int64_t m_bound = (tokens + C::BM - 1) / C::BM + experts;
-    *n_blocks = m_bound * *n_tiles;
-    const int64_t grid = (*n_blocks + kXcds - 1) / kXcds * kXcds;
-    return grid < (static_cast<int64_t>(1) << 31) ? grid : 0;
-}
-
 template <class C>
 int launch_grouped(const uint16_t* a, const uint16_t* w_gate, const uint16_t* w_up, const int32_t* offs,
-                   const float* probs, uint16_t* y, uint16_t* x_out, int64_t tokens, int64_t hidden, int64_t inter,
-                   int64_t experts, float limit, hipStream_t st) {
+                       const float* probs, uint16_t* y, uint16_t* x_out, int64_t tokens, int64_t hidden,
+                       int64_t inter, int64_t experts, float limit, hipStream_t st) {
     int64_t n_tiles, n_blocks;
     const int64_t grid = grouped_grid<C>(tokens, inter, experts, &n_tiles, &n_blocks);
     if (grid == 0) return MOE_EPI_ERR_BAD_SHAPE;
     (void)hipGetLastError();
     if (x_out)
-        hipLaunchKernelGGL((grouped_gate_up_swiglu_kernel<C, true>), dim3(static_cast<unsigned>(grid)),
-                           dim3(C::kThreads), 0, st, a, w_gate, w_up, offs, probs, y, x_out, tokens, hidden, inter,
-                           experts, limit, n_tiles, n_blocks);
+        hipLaunchKernelGGL((grouped_gate_up_swiglu_kernel<C, true>), dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0, st,
+                           a, w_gate, w_up, offs, probs, y, x_out, tokens, hidden, inter, experts, limit, n_tiles,
+                           n_blocks);
     else
-        hipLaunchKernelGGL((grouped_gate_up_swiglu_kernel<C, false>), dim3(static_cast<unsigned>(grid)),
-                           dim3(C::kThreads), 0, st, a, w_gate, w_up, offs, probs, y, x_out, tokens, hidden, inter,
-                           experts, limit, n_tiles, n_blocks);
+        hipLaunchKernelGGL((grouped_gate_up_swiglu_kernel<C, false>), dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0,
+                           st, a, w_gate, w_up, offs, probs, y, x_out, tokens, hidden, inter, experts, limit, n_tiles,
+                           n_blocks);
     return launch_status();
 }
 
