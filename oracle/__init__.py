@@ -310,3 +310,47 @@ def grouped_swiglu_fwd(a, w_gate, w_up, offs, probs, tokens, hidden, inter, expe
                                              _vp(scratch), tokens, hidden, inter, experts, float(L),
                                              threads or default_threads())
     return y, x
+
+
+# ---- down projection with the router-weight multiply, and the combine -------
+
+def _next3_lib():
+    lib = _grouped_lib()
+    if not getattr(lib, "_next3_ready", False):
+        vp = ctypes.c_void_p
+        lib.oracle_grouped_down_router_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, _i64, _i64, _i64, _i64,
+                                                       ctypes.c_int]
+        lib.oracle_grouped_down_router_fwd.restype = None
+        lib.oracle_moe_combine.argtypes = [vp, ctypes.c_int, vp, vp, _i64, _i64, _i64, _i64, ctypes.c_int]
+        lib.oracle_moe_combine.restype = None
+        lib._next3_ready = True
+    return lib
+
+
+def grouped_down_router_fwd(h, w_down, offs, probs, tokens, inter, hidden, experts, out_dtype=BF16, out_init=None,
+                            threads=None):
+    """out [tokens, hidden] (bf16 bits or float32): round_out(fp32(bf16(h @ w_down[e]^T)) * p) per expert's
+    rows; rows of no expert keep out_init (default: 0xFFFF bits / NaN)."""
+    h = _arr(h, np.uint16, (tokens, inter))
+    w_down = _arr(w_down, np.uint16, (experts, hidden, inter))
+    offs = _arr(offs, np.int32, (experts,))
+    probs = _arr(probs, np.float32, (tokens,))
+    if out_init is not None:
+        out = np.array(out_init, dtype=_NP[out_dtype])
+    elif out_dtype == BF16:
+        out = np.full((tokens, hidden), 0xFFFF, np.uint16)
+    else:
+        out = np.full((tokens, hidden), np.nan, np.float32)
+    _next3_lib().oracle_grouped_down_router_fwd(_vp(h), _vp(w_down), _vp(offs), _vp(probs), _vp(out), out_dtype,
+                                                tokens, inter, hidden, experts, threads or default_threads())
+    return out
+
+
+def moe_combine(expert_out, eo_dtype, row_of, rows, tokens, top_k, hidden, threads=None):
+    """float32 [tokens, hidden]: per token, the binary32 sum in ascending slot order of its rows of expert_out."""
+    expert_out = _arr(expert_out, _NP[eo_dtype], (rows, hidden))
+    row_of = _arr(row_of, np.int32, (tokens, top_k))
+    out = np.empty((tokens, hidden), np.float32)
+    _next3_lib().oracle_moe_combine(_vp(expert_out), eo_dtype, _vp(row_of), _vp(out), rows, tokens, top_k, hidden,
+                                    threads or default_threads())
+    return out

@@ -510,3 +510,78 @@ void oracle_grouped_swiglu_fwd(const uint16_t *a, const uint16_t *w_gate, const 
         start = end;
     }
 }
+
+/* ---- down projection with the router-weight multiply, and the combine --- */
+/*
+ * Sources:
+ *   [MK] (above): the routed down weights are contiguous bfloat16
+ *        [local_experts, hidden, expert_intermediate].
+ *   [RW] (above), _apply_router_weight_fp32: the expert down-projection
+ *        outputs [tokens, hidden] are multiplied by the permuted routing
+ *        probabilities in fp32 and cast to the output dtype (the activation
+ *        dtype, or fp32 where expert outputs are combined by scatter-add).
+ *   [GX] nemo_automodel.components.moe.quantized_experts,
+ *        GroupedExpertsMXFP4.forward: the local experts' contribution is an
+ *        fp32 [tokens, hidden] tensor, formed before the expert-parallel
+ *        reduction from each token's top-k routing slots.
+ *
+ * Down projection: for a row t of local expert e (rows grouped as in [GM],
+ * offs read as above), out2[t, n] = bf16(sum_i h[t, i] * w_down[e, n, i])
+ * (exact sum, rounded once: the grouped GEMM's output in the activation
+ * dtype), then out[t, n] = round_out(fp32(out2[t, n]) * p[t]) as in [RW].
+ *
+ * Combine: out[t, :] = sum over slots j = 0 .. top_k-1 with a row r =
+ * row_of[t, j] in [0, rows) of fp32(expert_out[r, :]), added in binary32 in
+ * ascending j (the pages leave the order of the scatter-add open; ascending
+ * slots is the reading taken, and makes the sum reproducible). A slot whose
+ * row is negative or out of range contributes nothing; a token with no such
+ * slot gets +0.
+ */
+
+/* [MK][GM][RW] out_dtype: ORACLE_BF16 or ORACLE_F32. Rows of no expert are not written. */
+void oracle_grouped_down_router_fwd(const uint16_t *h, const uint16_t *w_down, const int32_t *offs,
+                                    const float *probs, void *out, int out_dtype, int64_t tokens,
+                                    int64_t inter, int64_t hidden, int64_t experts, int nthreads)
+{
+    int64_t start = 0;
+    for (int64_t e = 0; e < experts; ++e) {
+        int64_t end = offs[e];
+        if (end < start) end = start;
+        if (end > tokens) end = tokens;
+        const uint16_t *w = w_down + e * hidden * inter;
+        int64_t t;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+        for (t = start; t < end; ++t) {
+            const uint16_t *ht = h + t * inter;
+            for (int64_t n = 0; n < hidden; ++n) {
+                const uint16_t *wn = w + n * inter;
+                double s = 0.0;
+                for (int64_t i = 0; i < inter; ++i)
+                    s += (double)oracle_bf16_to_f32(ht[i]) * (double)oracle_bf16_to_f32(wn[i]);
+                float out2 = oracle_bf16_to_f32(oracle_f64_to_bf16(s));
+                oracle_store(out, t * hidden + n, out_dtype, out2 * probs[t]);
+            }
+        }
+        start = end;
+    }
+}
+
+/* [GX] expert_out is [rows, hidden] of eo_dtype (bfloat16 or float32); row_of
+ * is [tokens, top_k]; out is float32 [tokens, hidden]. */
+void oracle_moe_combine(const void *expert_out, int eo_dtype, const int32_t *row_of, float *out,
+                        int64_t rows, int64_t tokens, int64_t top_k, int64_t hidden, int nthreads)
+{
+    int64_t t;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (t = 0; t < tokens; ++t) {
+        for (int64_t n = 0; n < hidden; ++n) {
+            float acc = 0.0f;
+            for (int64_t j = 0; j < top_k; ++j) {
+                int64_t r = row_of[t * top_k + j];
+                if (r >= 0 && r < rows)
+                    acc = acc + oracle_load(expert_out, r * hidden + n, eo_dtype);
+            }
+            out[t * hidden + n] = acc;
+        }
+    }
+}

@@ -19,6 +19,7 @@ from oracle import build as oracle_build
 from tests import test_oracle_pins as pins
 from tests import test_oracle_pins_dtypes as dpins
 from tests import test_oracle_pins_grouped as gpins
+from tests import test_oracle_pins_next3 as npins
 
 SRC = oracle_build.SRC
 
@@ -75,6 +76,18 @@ MUTANTS = [
     ("grouped: decreasing counts not clamped", "if (end < start) end = start;", ";"),
     ("grouped: sums rounded through binary32", "uint16_t g = oracle_f64_to_bf16(sum_scratch[t * 2 * inter + j]);",
      "uint16_t g = oracle_f32_to_bf16((float)sum_scratch[t * 2 * inter + j]);"),
+    ("down: probability not applied", "oracle_store(out, t * hidden + n, out_dtype, out2 * probs[t]);",
+     "oracle_store(out, t * hidden + n, out_dtype, out2);"),
+    ("down: sum not rounded to bf16 first", "float out2 = oracle_bf16_to_f32(oracle_f64_to_bf16(s));",
+     "float out2 = (float)s;"),
+    ("down: weights read transposed",
+     "s += (double)oracle_bf16_to_f32(ht[i]) * (double)oracle_bf16_to_f32(wn[i]);",
+     "s += (double)oracle_bf16_to_f32(ht[i]) * (double)oracle_bf16_to_f32(w[i * hidden + n]);"),
+    ("combine: slots in descending order", "for (int64_t j = 0; j < top_k; ++j) {",
+     "for (int64_t j = top_k - 1; j >= 0; --j) {"),
+    ("combine: starts from -0", "float acc = 0.0f;", "float acc = -0.0f;"),
+    ("combine: the last slot overwrites", "acc = acc + oracle_load(expert_out, r * hidden + n, eo_dtype);",
+     "acc = oracle_load(expert_out, r * hidden + n, eo_dtype);"),
     ("typed backward reads grad_y as x's neighbour",
      "oracle_load(grad_y, r * inter + j, dtype), L, q);", "oracle_load(x, r * inter + j, dtype), L, q);"),
 ]
@@ -118,6 +131,13 @@ def _pins():
         ("grouped per-expert scale", lambda o: gpins.test_per_expert_power_of_two_weights_select_the_expert(o)),
         ("grouped epilogue", lambda o: gpins.test_forward_is_the_epilogue_of_the_rounded_sums(o)),
         ("grouped tie", lambda o: gpins.test_sums_next_to_a_bf16_tie_are_rounded_once(o)),
+        ("down integer", lambda o: [npins.test_down_integer_products_and_power_of_two_probs(d, f, o)
+                                    for d in (real_oracle.BF16, real_oracle.F32) for f in ([4, 4, 11], [11, 3, 20])]),
+        ("down rational", lambda o: npins.test_down_exact_rational_sums_then_the_router_multiply(o)),
+        ("down layout", lambda o: npins.test_down_weights_are_rows_of_hidden(o)),
+        ("combine order", lambda o: npins.test_combine_adds_slots_in_ascending_order_in_binary32(o)),
+        ("combine integer", lambda o: [npins.test_combine_integer_rows_match_numpy(d, o)
+                                       for d in (real_oracle.BF16, real_oracle.F32)]),
     ]
     return calls
 
