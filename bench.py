@@ -31,6 +31,12 @@ Prints one JSON line. Options:
                      value in TFLOP/s of the two products, roofline against
                      the dense bf16 MFMA peak
   --no-x             grouped: write y only
+  --workload down_*  the down-projection grouped GEMM with the router-weight
+                     multiply fused into it (bf16 or fp32 output, as the
+                     workload names): TFLOP/s of the product, MFMA roofline
+  --workload combine_* the fp32 combine of routed rows into tokens: HBM GB/s
+                     of the local rows read once, row_of read once and the
+                     output written once
   --copy-calibration time a 1 GiB device-to-device copy instead (torch's copy_,
                      carried out by the HIP runtime's copy kernel): the plain
                      copy of known size whose FETCH_SIZE / WRITE_SIZE readings
@@ -55,6 +61,8 @@ METRICS = {
     "swiglu": "achieved HBM GB/s (% of MI355X peak), clamped-SwiGLU fwd+bwd at 131072×4096 bf16",
     "router": "achieved HBM GB/s (% of MI355X peak), fp32 router-weight multiply fwd+bwd",
     "grouped": "achieved TFLOP/s (% of MI355X dense bf16 peak), gate_up grouped GEMM + clamped SwiGLU epilogue",
+    "down": "achieved TFLOP/s (% of MI355X dense bf16 peak), down-projection grouped GEMM + router-weight multiply",
+    "combine": "achieved HBM GB/s (% of MI355X peak), fp32 combine of routed rows into tokens",
 }
 
 
@@ -82,6 +90,8 @@ KERNEL_SOURCES = {
     "swiglu": ("swiglu_clamped.hip", "swiglu_math.h", "epi_common.h"),
     "router": ("router_weight_mul.hip", "epi_common.h"),
     "grouped": ("grouped_swiglu.hip", "swiglu_math.h", "epi_common.h"),
+    "down": ("grouped_swiglu.hip", "swiglu_math.h", "epi_common.h"),
+    "combine": ("moe_combine.hip", "epi_common.h"),
 }
 
 
@@ -102,11 +112,27 @@ def kernel_source_digest(op: str) -> str:
 PROFILE_FOR = {"swiglu": "swiglu_clamped", "router": "router_weight_mul"}
 
 
+def op_of(workload) -> str:
+    from moe_routed_expert_amd.workloads import CombineWorkload, DownWorkload, GroupedWorkload
+    if isinstance(workload, GroupedWorkload):
+        return "grouped"
+    if isinstance(workload, DownWorkload):
+        return "down"
+    if isinstance(workload, CombineWorkload):
+        return "combine"
+    return workload.op
+
+
 def profile_name(workload) -> str:
     """The committed rocprofv3 summary that covers a workload's kernels."""
-    if hasattr(workload, "experts"):  # the grouped GEMM + epilogue
+    op = op_of(workload)
+    if op == "grouped":
         return "grouped_gate_up_swiglu_" + workload.name[len("grouped_"):] + ".md"
-    return f"{PROFILE_FOR[workload.op]}_{workload.rows}x{workload.cols}.md"
+    if op == "down":
+        return "grouped_down_router_" + workload.name[len("down_"):] + ".md"
+    if op == "combine":
+        return "moe_combine_" + workload.name[len("combine_"):] + ".md"
+    return f"{PROFILE_FOR[op]}_{workload.rows}x{workload.cols}.md"
 
 
 def load_traffic(kernel: str, workload) -> float | None:
@@ -123,8 +149,7 @@ def load_traffic(kernel: str, workload) -> float | None:
         return None
     block = text[start + len("```json"):text.find("```", start + 7)]
     rec = json.loads(block)
-    op = "grouped" if hasattr(workload, "experts") else workload.op
-    if rec.get("kernel_source_digest") != kernel_source_digest(op):
+    if rec.get("kernel_source_digest") != kernel_source_digest(op_of(workload)):
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
@@ -174,9 +199,13 @@ def main():
     if args.copy_calibration:
         return copy_calibration(args)
 
-    from moe_routed_expert_amd.workloads import GROUPED_WORKLOADS
+    from moe_routed_expert_amd.workloads import COMBINE_WORKLOADS, DOWN_WORKLOADS, GROUPED_WORKLOADS
     if args.workload in GROUPED_WORKLOADS:
         return grouped_main(args, GROUPED_WORKLOADS[args.workload])
+    if args.workload in DOWN_WORKLOADS:
+        return down_main(args, DOWN_WORKLOADS[args.workload])
+    if args.workload in COMBINE_WORKLOADS:
+        return combine_main(args, COMBINE_WORKLOADS[args.workload])
     w = WORKLOADS[args.workload or HEADLINE]
     dt = args.dtype
     od = (args.out_dtype or dt) if w.op == "router" else dt
@@ -400,6 +429,185 @@ def grouped_main(args, w):
                    "io": "bf16 a / weights / y / x, fp32 probs; bf16 MFMA products, fp32 accumulation",
                    "flops_per_step": flops},
         "frac_of_peak": value / PEAK_BF16_TFLOPS,
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def time_launches(step, args):
+    """Warm up, then time args.steps launches: (per-launch ms from HIP events on the launch
+    stream, wall ms per step)."""
+    import numpy as np
+    import torch
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return np.array([e0.elapsed_time(e1) for e0, e1 in evs]), wall * 1e3 / args.steps
+
+
+def oracle_timed(run, seconds):
+    """Whole passes of run() until `seconds` are spent (at least one, at most 100): (passes, s)."""
+    passes, t = 0, time.perf_counter()
+    while True:
+        run()
+        passes += 1
+        ct = time.perf_counter() - t
+        if ct >= seconds or passes >= 100:
+            return passes, ct
+
+
+def down_main(args, w):
+    """One step = one fused down-projection grouped GEMM + router multiply launch."""
+    import numpy as np
+    import torch
+
+    import moe_routed_expert_amd as epi
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    d = w.generate()
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    h, wd = bf(d["h"]), bf(d["w_down"])
+    offs = torch.from_numpy(d["offs"]).to(dev)
+    p = torch.from_numpy(d["probs"]).to(dev)
+    out = torch.empty((w.tokens, w.hidden), dtype=torch.float32 if w.out_dtype == "f32" else torch.bfloat16,
+                      device=dev)
+    ms, ms_per_step = time_launches(lambda: epi.grouped_down_router_fwd(h, wd, offs, p, out), args)
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    avg_ms = float(ms.mean())
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    name = "grouped_down_router_fwd"
+    kernels = {name: {"avg_us": avg_ms * 1e3, "median_us": float(np.median(ms)) * 1e3, "min_us": float(ms.min()) * 1e3,
+                      "flops": flops, "TFLOP/s": achieved, "frac_of_peak": achieved / PEAK_BF16_TFLOPS,
+                      "min_hbm_bytes": w.min_bytes()}}
+    roofline = {"bound": "mfma", "kernel": name, "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": load_traffic(name, w), "flops_per_launch": flops}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = args.cpu_threads or oracle.default_threads()
+        # sample: the first 8 rows of every expert, regrouped with their own counts
+        ends = d["offs"].astype(np.int64)
+        starts = np.concatenate([[0], ends[:-1]])
+        idx = np.concatenate([np.arange(s0, min(s0 + 8, e0)) for s0, e0 in zip(starts, ends)]).astype(np.int64)
+        sub_offs = np.cumsum([min(8, max(0, e0 - s0)) for s0, e0 in zip(starts, ends)]).astype(np.int32)
+        sh, sp = d["h"][idx], d["probs"][idx]
+        code = oracle.F32 if w.out_dtype == "f32" else oracle.BF16
+        print(f"[bench] oracle on the host ({threads} threads): {idx.size} sampled rows per pass for >= "
+              f"{args.cpu_seconds:g} s", file=sys.stderr, flush=True)
+        passes, ct = oracle_timed(lambda: oracle.grouped_down_router_fwd(
+            sh, d["w_down"], sub_offs, sp, idx.size, w.inter, w.hidden, w.experts, out_dtype=code, threads=threads),
+            args.cpu_seconds)
+        sample_flops = 2 * idx.size * w.inter * w.hidden
+        cpu = {"value": passes * sample_flops / ct / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "sample": f"{passes} passes over {idx.size} rows (the first 8 of each expert), {ct:.1f} s"}
+
+    line = {
+        "metric": METRICS["down"] + f" ({w.name})",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": "down", "tokens": w.tokens, "inter": w.inter, "hidden": w.hidden,
+                   "experts": w.experts, "output": w.out_dtype,
+                   "io": f"bf16 h / weights, fp32 probs, {w.out_dtype} out; bf16 MFMA products, fp32 accumulation",
+                   "flops_per_step": flops},
+        "frac_of_peak": value / PEAK_BF16_TFLOPS,
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def combine_main(args, w):
+    """One step = one combine launch over every token."""
+    import numpy as np
+    import torch
+
+    import moe_routed_expert_amd as epi
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    d = w.generate()
+    eo_np, row_of, rows = d["expert_out"], d["row_of"], d["rows"]
+    if w.eo_dtype == "f32":
+        eo = torch.from_numpy(eo_np).to(dev)
+    else:
+        eo = torch.from_numpy(eo_np.view(np.int16)).view(
+            torch.bfloat16 if w.eo_dtype == "bf16" else torch.float16).to(dev)
+    ro = torch.from_numpy(row_of).to(dev)
+    out = torch.empty((w.tokens, w.hidden), dtype=torch.float32, device=dev)
+    ms, ms_per_step = time_launches(lambda: epi.moe_combine_fwd(eo, ro, out), args)
+    nbytes = w.min_bytes(row_of, rows)
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    avg_ms = float(ms.mean())
+    gbs = nbytes / (avg_ms * 1e-3) / 1e9
+    name = "moe_combine_fwd"
+    kernels = {name: {"avg_us": avg_ms * 1e3, "median_us": float(np.median(ms)) * 1e3, "min_us": float(ms.min()) * 1e3,
+                      "algorithmic_bytes": nbytes, "GB/s": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS}}
+    roofline = {"bound": "hbm", "kernel": name, "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS, "traffic": load_traffic(name, w), "algorithmic_bytes_per_launch": nbytes}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = args.cpu_threads or oracle.default_threads()
+        sample = min(w.tokens, 4096)
+        code = {"bf16": oracle.BF16, "f16": oracle.F16, "f32": oracle.F32}[w.eo_dtype]
+        eo_o = eo_np.view(np.float16) if w.eo_dtype == "f16" else eo_np
+        sro = np.ascontiguousarray(row_of[:sample])
+        print(f"[bench] oracle on the host ({threads} threads): {sample} tokens per pass for >= "
+              f"{args.cpu_seconds:g} s", file=sys.stderr, flush=True)
+        passes, ct = oracle_timed(lambda: oracle.moe_combine(eo_o, code, sro, rows, sample, w.top_k, w.hidden,
+                                                             threads=threads), args.cpu_seconds)
+        valid = int(((sro >= 0) & (sro < rows)).sum())
+        sample_bytes = valid * w.hidden * eo_np.itemsize + sro.size * 4 + sample * w.hidden * 4
+        cpu = {"value": passes * sample_bytes / ct / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"{passes} passes over the first {sample} tokens, {ct:.1f} s"}
+
+    line = {
+        "metric": METRICS["combine"] + f" ({w.name})",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": "combine", "tokens": w.tokens, "hidden": w.hidden, "top_k": w.top_k,
+                   "global_experts": w.global_experts, "local_experts": w.local_experts, "rows": rows,
+                   "expert_out": w.eo_dtype, "io": f"{w.eo_dtype} routed rows, int32 row_of, fp32 out; fp32 adds",
+                   "bytes_per_step": nbytes},
+        "frac_of_peak": value / PEAK_HBM_GBS,
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -197,6 +197,67 @@ int grouped_gate_up_swiglu_fwd(const uint16_t *a, const uint16_t *w_gate, const 
                                int64_t tokens, int64_t hidden, int64_t inter, int64_t experts, float limit,
                                void *stream);
 
+/*
+ * Down projection grouped GEMM with the router-weight multiply fused into it
+ * (the step after the SwiGLU epilogue, and the router multiply above, in one
+ * kernel). Defined by:
+ *   "nemo_automodel.components.moe.mok_experts": the routed down weights are
+ *     contiguous bf16 [local_experts, hidden, expert_intermediate];
+ *   "nemo_automodel.components.moe.quantized_experts",
+ *     MXFP4ExpertStorageMixin._mxfp4_base_mm: grouped rows and offs as for
+ *     grouped_gate_up_swiglu_fwd, the product in the activation dtype;
+ *   "nemo_automodel.components.moe.optimized_ops", _apply_router_weight_fp32:
+ *     that product times the permuted probability in float32, cast to the
+ *     output dtype (float32 when the outputs are then combined by
+ *     scatter-add).
+ * Rows of expert e as for grouped_gate_up_swiglu_fwd. For such a row t:
+ *   out2[t, n] = bf16( sum_i h[t, i] * w_down[e, n, i] )   (float32 accumulation)
+ *   out[t, n]  = out_dtype( float32(out2[t, n]) * probs[t] )
+ * i.e. router_weight_mul_fwd_typed of out2. Rows at or past the last end are
+ * not written.
+ *   h          [tokens, inter] bf16                 in, rows grouped by expert
+ *   w_down     [experts, hidden, inter] bf16        in
+ *   offs       [experts] int32, device memory       in (read on the device only)
+ *   probs      [tokens] float32                     in
+ *   out        [tokens, hidden] of out_dtype        out
+ *   out_dtype  MOE_EPI_BF16 or MOE_EPI_F32 (MOE_EPI_ERR_BAD_DTYPE otherwise)
+ * inter and hidden must be multiples of 8 (MOE_EPI_ERR_BAD_SHAPE otherwise),
+ * tokens at most INT32_MAX; h, w_down and out 16-byte aligned, offs and probs
+ * 4-byte aligned (MOE_EPI_ERR_MISALIGNED); out may not overlap any input
+ * (MOE_EPI_ERR_ALIAS). The caller owns every buffer; the library allocates
+ * nothing and queues the work on `stream`. Returns a moe_epi_status.
+ */
+int grouped_down_router_fwd(const uint16_t *h, const uint16_t *w_down, const int32_t *offs,
+                            const float *probs, void *out, int out_dtype, int64_t tokens, int64_t inter,
+                            int64_t hidden, int64_t experts, void *stream);
+
+/*
+ * Combine of the routed rows back into tokens: per token, the float32 sum of
+ * its top-k routed rows that this rank holds. Defined by
+ * "nemo_automodel.components.moe.quantized_experts",
+ * GroupedExpertsMXFP4.forward (the local experts' float32 [tokens, hidden]
+ * contribution, summed over each token's top-k slots; slots routed to other
+ * ranks' experts add nothing) and "nemo_automodel.components.moe
+ * .optimized_ops", _apply_router_weight_fp32 (the rows are float32 for this
+ * combine). For token t:
+ *   out[t, :] = +0 + expert_out[row_of[t, 0], :] + ... + expert_out[row_of[t, top_k-1], :]
+ * as binary32 additions in ascending slot order, skipping every slot whose
+ * row index is outside [0, rows) (a slot of another rank's expert, or none).
+ * The result is bit-exact: the same binary32 operations in the same order for
+ * every element.
+ *   expert_out [rows, hidden] of eo_dtype          in (may be NULL if rows == 0)
+ *   eo_dtype   MOE_EPI_BF16, MOE_EPI_F16 or MOE_EPI_F32
+ *   row_of     [tokens, top_k] int32                in, routed row of each slot
+ *   out        [tokens, hidden] float32            out, every element written
+ * hidden must be a multiple of 8, top_k in [1, 1024] (MOE_EPI_ERR_BAD_SHAPE
+ * otherwise); expert_out and out 16-byte aligned, row_of 4-byte aligned
+ * (MOE_EPI_ERR_MISALIGNED); out may not overlap an input (MOE_EPI_ERR_ALIAS).
+ * tokens == 0 launches nothing. The caller owns every buffer; the library
+ * allocates nothing and queues the work on `stream`. Returns a moe_epi_status.
+ */
+int moe_combine_fwd(const void *expert_out, int eo_dtype, const int32_t *row_of, float *out, int64_t rows,
+                    int64_t tokens, int64_t top_k, int64_t hidden, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *moe_epi_status_string(int status);
 

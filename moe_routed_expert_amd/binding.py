@@ -12,6 +12,9 @@ Names follow the C ABI (include/moe_epi.h):
   swiglu_clamped_bwd(x, probs, grad_y, grad_x, grad_probs, limit)
   router_weight_mul_fwd(x, probs, out)
   router_weight_mul_bwd(grad_out, x, probs, grad_x, grad_probs)
+  grouped_gate_up_swiglu_fwd(a, w_gate, w_up, offs, probs, y, x_out, limit)
+  grouped_down_router_fwd(h, w_down, offs, probs, out)
+  moe_combine_fwd(expert_out, row_of, out)
 plus allocating helpers and torch.autograd.Function wrappers with the shapes
 of the pages' SwigluClamped / _RouterWeightMulFunction.
 """
@@ -68,9 +71,12 @@ def lib() -> ctypes.CDLL:
     L.router_weight_mul_fwd_typed.argtypes = [vp, i32, vp, vp, i32, i64, i64, vp]
     L.router_weight_mul_bwd_typed.argtypes = [vp, i32, vp, i32, vp, vp, vp, i64, i64, vp]
     L.grouped_gate_up_swiglu_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp]
+    L.grouped_down_router_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, vp]
+    L.moe_combine_fwd.argtypes = [vp, i32, vp, vp, i64, i64, i64, i64, vp]
     for name in ("swiglu_clamped_fwd", "swiglu_clamped_bwd", "router_weight_mul_fwd", "router_weight_mul_bwd",
                  "swiglu_clamped_fwd_typed", "swiglu_clamped_bwd_typed", "router_weight_mul_fwd_typed",
-                 "router_weight_mul_bwd_typed", "grouped_gate_up_swiglu_fwd"):
+                 "router_weight_mul_bwd_typed", "grouped_gate_up_swiglu_fwd", "grouped_down_router_fwd",
+                 "moe_combine_fwd"):
         getattr(L, name).restype = ctypes.c_int
     L.moe_epi_status_string.argtypes = [ctypes.c_int]
     L.moe_epi_status_string.restype = ctypes.c_char_p
@@ -230,6 +236,46 @@ def grouped_gate_up_swiglu_fwd(a, w_gate, w_up, offs, probs, y, x_out, limit: fl
                                               probs.data_ptr(), y.data_ptr(), _ptr(x_out), tokens, hidden, inter,
                                               experts, float(limit), st)
     _check(status, "grouped_gate_up_swiglu_fwd")
+
+
+def grouped_down_router_fwd(h, w_down, offs, probs, out, stream=None) -> None:
+    """Fused down-projection grouped GEMM + router-weight multiply. h [tokens, inter] bf16 (rows grouped
+    by expert); w_down [experts, hidden, inter] bf16; offs int32 [experts] cumulative token counts (on the
+    device); probs fp32 [tokens] or [tokens, 1]; out [tokens, hidden] bf16 or fp32:
+    out = out.dtype(fp32(bf16(h @ w_down[e]^T)) * probs)."""
+    tokens, inter = _rows_cols(h, "h")
+    if w_down.dim() != 3:
+        raise ValueError(f"w_down must be 3-D [experts, hidden, inter], got {tuple(w_down.shape)}")
+    experts, hidden = int(w_down.shape[0]), int(w_down.shape[1])
+    dev = h.device
+    _need(h, "h", torch.bfloat16, [(tokens, inter)], dev)
+    _need(w_down, "w_down", torch.bfloat16, [(experts, hidden, inter)], dev)
+    _need(offs, "offs", torch.int32, [(experts,)], dev)
+    _need(probs, "probs", torch.float32, [(tokens,), (tokens, 1)], dev)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"out: expected bfloat16 or float32, got {out.dtype}")
+    _need(out, "out", out.dtype, [(tokens, hidden)], dev)
+    st = _stream_handle(h, stream)
+    status = lib().grouped_down_router_fwd(h.data_ptr(), w_down.data_ptr(), offs.data_ptr(), probs.data_ptr(),
+                                           out.data_ptr(), DTYPE_CODE[out.dtype], tokens, inter, hidden, experts,
+                                           st)
+    _check(status, "grouped_down_router_fwd")
+
+
+def moe_combine_fwd(expert_out, row_of, out, stream=None) -> None:
+    """out[t] = fp32 sum, in ascending slot order from +0, of expert_out[row_of[t, j]] over the slots j
+    whose row is in [0, rows). expert_out [rows, hidden] bf16, fp16 or fp32; row_of int32 [tokens, top_k];
+    out fp32 [tokens, hidden]."""
+    rows, hidden = _rows_cols(expert_out, "expert_out")
+    tokens, top_k = _rows_cols(row_of, "row_of")
+    dev = out.device
+    _need(expert_out, "expert_out", expert_out.dtype, [(rows, hidden)], dev)
+    _need(row_of, "row_of", torch.int32, [(tokens, top_k)], dev)
+    _need(out, "out", torch.float32, [(tokens, hidden)], dev)
+    st = _stream_handle(out, stream)
+    status = lib().moe_combine_fwd(_ptr(expert_out) if rows else None, _code(expert_out, "expert_out"),
+                                   row_of.data_ptr(), out.data_ptr(), rows, tokens, top_k, hidden, st)
+    _check(status, "moe_combine_fwd")
 
 
 # ---- allocating helpers and autograd wrappers ------------------------------

@@ -141,8 +141,9 @@ __device__ __forceinline__ void store_tile(const uint16_t* stage, uint16_t* __re
 // tiles, rounded up to a multiple of the XCD count. Returns 0 when it does not
 // fit a 1-D grid.
 template <class C>
-int64_t grouped_grid(int64_t tokens, int64_t inter, int64_t experts, int64_t* n_tiles, int64_t* n_blocks) {
-    *n_tiles = (inter + C::BN - 1) / C::BN;
+int64_t grouped_grid(int64_t tokens, int64_t n_cols, int64_t cols_per_tile, int64_t experts, int64_t* n_tiles,
+                     int64_t* n_blocks) {
+    *n_tiles = (n_cols + cols_per_tile - 1) / cols_per_tile;
     const int64_t m_bound = (tokens + C::BM - 1) / C::BM + experts;
     *n_blocks = m_bound * *n_tiles;
     const int64_t grid = (*n_blocks + kXcds - 1) / kXcds * kXcds;
@@ -234,28 +235,42 @@ __device__ __forceinline__ void wait_loads_but() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
-template <class C, bool kWriteX>
-__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::OCC))) void grouped_gate_up_swiglu_kernel(
-    const uint16_t* __restrict__ a, const uint16_t* __restrict__ w_gate, const uint16_t* __restrict__ w_up,
-    const int32_t* __restrict__ offs, const float* __restrict__ probs, uint16_t* __restrict__ y,
-    uint16_t* __restrict__ x_out, int64_t tokens, int64_t hidden, int64_t inter, int64_t experts, float L,
+// Epilogues: the clamped SwiGLU of (gate, up) (two weight tensors, the same
+// columns of each), or the router-weight multiply of a single weight tensor's
+// output (the block's two weight tiles are then consecutive column ranges of
+// it), stored as bf16 or fp32.
+enum class Epi { kSwiglu, kRouterBf16, kRouterF32 };
+
+// A grouped GEMM over rows grouped by expert: the reduction runs over k_dim
+// (hidden for gate_up, inter for the down projection); n_dim is the width of
+// each weight tensor's output (inter for gate_up, hidden for down).
+template <class C, Epi kEpi, bool kWriteX>
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::OCC))) void grouped_gemm_kernel(
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w2,
+    const int32_t* __restrict__ offs, const float* __restrict__ probs, void* __restrict__ out,
+    uint16_t* __restrict__ x_out, int64_t tokens, int64_t k_dim, int64_t n_dim, int64_t experts, float L,
     int64_t n_tiles, int64_t n_blocks) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[C::kLdsElems];
     constexpr int MI = C::MI, NI = C::NI, S = C::S;
+    constexpr bool kRouter = kEpi != Epi::kSwiglu;
 
     const int64_t per = static_cast<int64_t>(gridDim.x) / kXcds;
     const int64_t logical = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
     if (logical >= n_blocks) return;
     int64_t mt, nt;
     tile_of(logical, n_blocks / n_tiles, n_tiles, C::GM, &mt, &nt);
-    const int64_t col0 = nt * C::BN;
     const TileRows tr = find_row_tile(offs, tokens, experts, mt, C::BM);
     if (tr.rows == 0) return;
-    const int ncols = static_cast<int>(inter - col0 < C::BN ? inter - col0 : C::BN);
+    // first output column of each weight tile (gate and up: the same columns;
+    // router: two consecutive ranges of one weight tensor) and its valid width
+    const int64_t col1 = nt * (kRouter ? 2 * C::BN : C::BN);
+    const int64_t col2 = kRouter ? col1 + C::BN : col1;
+    const int ncols1 = static_cast<int>(n_dim - col1 < C::BN ? n_dim - col1 : C::BN);
+    const int ncols2 = static_cast<int>(n_dim - col2 <= 0 ? 0 : (n_dim - col2 < C::BN ? n_dim - col2 : C::BN));
 
-    const uint16_t* a_tile = a + tr.row0 * hidden;
-    const uint16_t* g_tile = w_gate + (tr.expert * inter + col0) * hidden;
-    const uint16_t* u_tile = w_up + (tr.expert * inter + col0) * hidden;
+    const uint16_t* a_tile = a + tr.row0 * k_dim;
+    const uint16_t* g_tile = w1 + (tr.expert * n_dim + col1) * k_dim;
+    const uint16_t* u_tile = w2 + (tr.expert * n_dim + (ncols2 > 0 ? col2 : col1)) * k_dim;  // unread if ncols2 == 0
 
     const int lane = static_cast<int>(threadIdx.x) % 64;
     const int wave = static_cast<int>(threadIdx.x) / 64;
@@ -270,18 +285,18 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
             acc_u[mi][ni] = f32x16{};
         }
 
-    const int64_t nk = (hidden + C::BK - 1) / C::BK;
+    const int64_t nk = (k_dim + C::BK - 1) / C::BK;
     // Every wavefront issues exactly kDmaPerStage loads per stage only when no
     // chunk of the tile lies outside the matrices (a wavefront whose chunk is
     // out of range for all its lanes skips that load); otherwise the waits
     // below fall back to waiting for every load.
-    const bool full = tr.rows == C::BM && ncols == C::BN && hidden % C::BK == 0;
+    const bool full = tr.rows == C::BM && ncols1 == C::BN && ncols2 == C::BN && k_dim % C::BK == 0;
     auto issue = [&](int64_t kt) {
         uint16_t* st = lds + (kt % S) * C::kStageElems;
         const int64_t k0 = kt * C::BK;
-        dma_tile<C, C::kAChunks>(st, a_tile, hidden, tr.rows, k0, hidden);
-        dma_tile<C, C::kWChunks>(st + C::kAElems, g_tile, hidden, ncols, k0, hidden);
-        dma_tile<C, C::kWChunks>(st + C::kAElems + C::kWElems, u_tile, hidden, ncols, k0, hidden);
+        dma_tile<C, C::kAChunks>(st, a_tile, k_dim, tr.rows, k0, k_dim);
+        dma_tile<C, C::kWChunks>(st + C::kAElems, g_tile, k_dim, ncols1, k0, k_dim);
+        dma_tile<C, C::kWChunks>(st + C::kAElems + C::kWElems, u_tile, k_dim, ncols2, k0, k_dim);
     };
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
@@ -339,63 +354,109 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     __syncthreads();  // all fragment reads done before the buffers become the staging tile
 
     uint16_t* stage = lds;
+    if constexpr (kEpi == Epi::kSwiglu) {
+        uint16_t* y = static_cast<uint16_t*>(out);
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int r = acc_row<C>(wm, mi, j, lane);
-            const float p = r < tr.rows ? probs[tr.row0 + r] : 0.0f;
+            for (int j = 0; j < 16; ++j) {
+                const int r = acc_row<C>(wm, mi, j, lane);
+                const float p = r < tr.rows ? probs[tr.row0 + r] : 0.0f;
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni) {
-                const float g = round_bf16(acc_g[mi][ni][j]);
-                const float u = round_bf16(acc_u[mi][ni][j]);
-                stage[r * C::kLdo + acc_col<C>(wn, ni, lane)] = to_bf16(fwd_elem(g, u, p, L));
+                for (int ni = 0; ni < NI; ++ni) {
+                    const float g = round_bf16(acc_g[mi][ni][j]);
+                    const float u = round_bf16(acc_u[mi][ni][j]);
+                    stage[r * C::kLdo + acc_col<C>(wn, ni, lane)] = to_bf16(fwd_elem(g, u, p, L));
+                }
             }
+        __syncthreads();
+        store_tile<C>(stage, y, n_dim, tr.row0, tr.rows, col1, n_dim);
+        if constexpr (kWriteX) {
+            __syncthreads();
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        stage[acc_row<C>(wm, mi, j, lane) * C::kLdo + acc_col<C>(wn, ni, lane)] =
+                            to_bf16(acc_g[mi][ni][j]);
+            __syncthreads();
+            store_tile<C>(stage, x_out, 2 * n_dim, tr.row0, tr.rows, col1, n_dim);
+            __syncthreads();
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        stage[acc_row<C>(wm, mi, j, lane) * C::kLdo + acc_col<C>(wn, ni, lane)] =
+                            to_bf16(acc_u[mi][ni][j]);
+            __syncthreads();
+            store_tile<C>(stage, x_out + n_dim, 2 * n_dim, tr.row0, tr.rows, col1, n_dim);
         }
-    __syncthreads();
-    store_tile<C>(stage, y, inter, tr.row0, tr.rows, col0, inter);
-    if constexpr (kWriteX) {
-        __syncthreads();
+    } else if constexpr (kEpi == Epi::kRouterF32) {
+        // fp32 straight from registers: for each register j a wavefront writes
+        // two rows x 32 consecutive floats, i.e. whole 128-byte lines
+        float* o = static_cast<float*>(out);
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni)
+            for (int j = 0; j < 16; ++j) {
+                const int r = acc_row<C>(wm, mi, j, lane);
+                if (r >= tr.rows) continue;
+                const float p = probs[tr.row0 + r];
+                float* orow = o + (tr.row0 + r) * n_dim;
 #pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    stage[acc_row<C>(wm, mi, j, lane) * C::kLdo + acc_col<C>(wn, ni, lane)] =
-                        to_bf16(acc_g[mi][ni][j]);
-        __syncthreads();
-        store_tile<C>(stage, x_out, 2 * inter, tr.row0, tr.rows, col0, inter);
-        __syncthreads();
+                for (int ni = 0; ni < NI; ++ni) {
+                    const int c = acc_col<C>(wn, ni, lane);
+                    if (c < ncols1) orow[col1 + c] = round_bf16(acc_g[mi][ni][j]) * p;
+                    if (c < ncols2) orow[col2 + c] = round_bf16(acc_u[mi][ni][j]) * p;
+                }
+            }
+    } else {
+        uint16_t* o = static_cast<uint16_t*>(out);
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
+        for (int half = 0; half < 2; ++half) {
+            if (half == 1) __syncthreads();  // the first half's stores have read the staging tile
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni)
+            for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    stage[acc_row<C>(wm, mi, j, lane) * C::kLdo + acc_col<C>(wn, ni, lane)] =
-                        to_bf16(acc_u[mi][ni][j]);
-        __syncthreads();
-        store_tile<C>(stage, x_out + inter, 2 * inter, tr.row0, tr.rows, col0, inter);
+                for (int j = 0; j < 16; ++j) {
+                    const int r = acc_row<C>(wm, mi, j, lane);
+                    const float p = r < tr.rows ? probs[tr.row0 + r] : 0.0f;
+#pragma unroll
+                    for (int ni = 0; ni < NI; ++ni) {
+                        const float v = half == 0 ? acc_g[mi][ni][j] : acc_u[mi][ni][j];
+                        stage[r * C::kLdo + acc_col<C>(wn, ni, lane)] = to_bf16(round_bf16(v) * p);
+                    }
+                }
+            __syncthreads();
+            if (half == 0)
+                store_tile<C>(stage, o, n_dim, tr.row0, tr.rows, col1, col1 + ncols1);
+            else if (ncols2 > 0)
+                store_tile<C>(stage, o, n_dim, tr.row0, tr.rows, col2, col2 + ncols2);
+        }
     }
 }
 
-template <class C>
-int launch_grouped(const uint16_t* a, const uint16_t* w_gate, const uint16_t* w_up, const int32_t* offs,
-                       const float* probs, uint16_t* y, uint16_t* x_out, int64_t tokens, int64_t hidden,
-                       int64_t inter, int64_t experts, float limit, hipStream_t st) {
+template <class C, Epi kEpi>
+int launch_grouped(const uint16_t* a, const uint16_t* w1, const uint16_t* w2, const int32_t* offs,
+                   const float* probs, void* out, uint16_t* x_out, int64_t tokens, int64_t k_dim, int64_t n_dim,
+                   int64_t experts, float limit, hipStream_t st) {
     int64_t n_tiles, n_blocks;
-    const int64_t grid = grouped_grid<C>(tokens, inter, experts, &n_tiles, &n_blocks);
+    const int64_t grid = grouped_grid<C>(tokens, n_dim, kEpi == Epi::kSwiglu ? C::BN : 2 * C::BN, experts, &n_tiles,
+                                         &n_blocks);
     if (grid == 0) return MOE_EPI_ERR_BAD_SHAPE;
     (void)hipGetLastError();
-    if (x_out)
-        hipLaunchKernelGGL((grouped_gate_up_swiglu_kernel<C, true>), dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0, st,
-                           a, w_gate, w_up, offs, probs, y, x_out, tokens, hidden, inter, experts, limit, n_tiles,
+    if (kEpi == Epi::kSwiglu && x_out)
+        hipLaunchKernelGGL((grouped_gemm_kernel<C, kEpi, true>), dim3(static_cast<unsigned>(grid)), dim3(C::kThreads),
+                           0, st, a, w1, w2, offs, probs, out, x_out, tokens, k_dim, n_dim, experts, limit, n_tiles,
                            n_blocks);
     else
-        hipLaunchKernelGGL((grouped_gate_up_swiglu_kernel<C, false>), dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0,
-                           st, a, w_gate, w_up, offs, probs, y, x_out, tokens, hidden, inter, experts, limit, n_tiles,
-                           n_blocks);
+        hipLaunchKernelGGL((grouped_gemm_kernel<C, kEpi, false>), dim3(static_cast<unsigned>(grid)),
+                           dim3(C::kThreads), 0, st, a, w1, w2, offs, probs, out, x_out, tokens, k_dim, n_dim, experts,
+                           limit, n_tiles, n_blocks);
     return launch_status();
 }
 
@@ -430,6 +491,35 @@ extern "C" int grouped_gate_up_swiglu_fwd(const uint16_t* a, const uint16_t* w_g
         if (overlaps(out, ra) || overlaps(out, rg) || overlaps(out, ru) || overlaps(out, ro) || overlaps(out, rp))
             return MOE_EPI_ERR_ALIAS;
     if (overlaps(ry, rx)) return MOE_EPI_ERR_ALIAS;
-    return launch_grouped<Prod>(a, w_gate, w_up, offs, probs, y, x_out, tokens, hidden, inter, experts, limit,
-                                as_stream(stream));
+    return launch_grouped<Prod, Epi::kSwiglu>(a, w_gate, w_up, offs, probs, y, x_out, tokens, hidden, inter, experts,
+                                              limit, as_stream(stream));
+}
+
+extern "C" int grouped_down_router_fwd(const uint16_t* h, const uint16_t* w_down, const int32_t* offs,
+                                       const float* probs, void* out, int out_dtype, int64_t tokens, int64_t inter,
+                                       int64_t hidden, int64_t experts, void* stream) {
+    if (out_dtype != MOE_EPI_BF16 && out_dtype != MOE_EPI_F32) return MOE_EPI_ERR_BAD_DTYPE;
+    if (tokens < 0 || tokens > INT32_MAX || inter <= 0 || hidden <= 0 || experts <= 0 || inter % 8 != 0 ||
+        hidden % 8 != 0)
+        return MOE_EPI_ERR_BAD_SHAPE;
+    if (experts > INT64_MAX / 4 / hidden)  // before experts * hidden is formed
+        return MOE_EPI_ERR_BAD_SHAPE;
+    const int eo = elem_bytes(out_dtype);
+    int64_t hb, wb, ob, pb, fb;
+    if (!bytes_ok(tokens, inter, 2, &hb) || !bytes_ok(experts * hidden, inter, 2, &wb) ||
+        !bytes_ok(tokens, hidden, eo, &ob) || !bytes_ok(tokens, 1, 4, &pb) || !bytes_ok(experts, 1, 4, &fb))
+        return MOE_EPI_ERR_BAD_SHAPE;
+    if (tokens == 0) return MOE_EPI_SUCCESS;
+    if (!h || !w_down || !offs || !probs || !out) return MOE_EPI_ERR_NULL_POINTER;
+    if (!aligned(h, 16) || !aligned(w_down, 16) || !aligned(out, 16) || !aligned(offs, 4) || !aligned(probs, 4))
+        return MOE_EPI_ERR_MISALIGNED;
+    const Range ro = range_of(out, ob);
+    if (overlaps(ro, range_of(h, hb)) || overlaps(ro, range_of(w_down, wb)) || overlaps(ro, range_of(offs, fb)) ||
+        overlaps(ro, range_of(probs, pb)))
+        return MOE_EPI_ERR_ALIAS;
+    if (out_dtype == MOE_EPI_F32)
+        return launch_grouped<Prod, Epi::kRouterF32>(h, w_down, w_down, offs, probs, out, nullptr, tokens, inter,
+                                                     hidden, experts, 1.0f, as_stream(stream));
+    return launch_grouped<Prod, Epi::kRouterBf16>(h, w_down, w_down, offs, probs, out, nullptr, tokens, inter, hidden,
+                                                  experts, 1.0f, as_stream(stream));
 }

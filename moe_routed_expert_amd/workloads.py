@@ -201,6 +201,22 @@ HEADLINE = "swiglu_131072x2048"
 #   - probs ~ U(0, 1) fp32.
 # Draws use their own SeedSequence streams (kinds 10-14), chunked like the rest.
 
+def expert_counts(seed: int, tokens: int, experts: int, split: str) -> np.ndarray:
+    """Tokens per local expert: a multinomial over Dirichlet(2) shares ("dirichlet"), the
+    same with one empty expert in the middle ("one_empty"), or as even as possible ("even")."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(10, 0))))
+    if split == "even":
+        c = np.full(experts, tokens // experts, dtype=np.int64)
+        c[: tokens % experts] += 1
+        return c
+    if split == "one_empty" and experts > 1:
+        c = g.multinomial(tokens, g.dirichlet(np.full(experts - 1, 2.0)))
+        return np.insert(c, experts // 2, 0)
+    if split not in ("dirichlet", "one_empty"):
+        raise ValueError(split)
+    return g.multinomial(tokens, g.dirichlet(np.full(experts, 2.0)))
+
+
 @dataclass(frozen=True)
 class GroupedWorkload:
     name: str
@@ -225,18 +241,7 @@ class GroupedWorkload:
         return t * h * 2 + 2 * e * i * h * 2 + 4 * t + 4 * e + t * i * 2 + (t * 2 * i * 2 if write_x else 0)
 
     def counts(self) -> np.ndarray:
-        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(self.seed, spawn_key=(10, 0))))
-        e = self.experts
-        if self.split == "even":
-            c = np.full(e, self.tokens // e, dtype=np.int64)
-            c[: self.tokens % e] += 1
-            return c
-        if self.split == "one_empty" and e > 1:
-            c = g.multinomial(self.tokens, g.dirichlet(np.full(e - 1, 2.0)))
-            return np.insert(c, e // 2, 0)
-        if self.split not in ("dirichlet", "one_empty"):
-            raise ValueError(self.split)
-        return g.multinomial(self.tokens, g.dirichlet(np.full(e, 2.0)))
+        return expert_counts(self.seed, self.tokens, self.experts, self.split)
 
     def offs(self) -> np.ndarray:
         return np.cumsum(self.counts()).astype(np.int32)
@@ -275,6 +280,160 @@ class GroupedWorkload:
         probs = rng(14, 0).random(t, dtype=np.float32)
         return {"a": a, "w_gate": w_gate, "w_up": w_up, "offs": self.offs(), "probs": probs}
 
+
+@dataclass(frozen=True)
+class DownWorkload:
+    """Down projection grouped GEMM + router-weight multiply: h [tokens, inter] (the SwiGLU
+    output, rows grouped by expert), w_down [experts, hidden, inter], probs [tokens].
+
+    h ~ N(0, h_sigma^2) and w ~ N(0, (out_sigma / (h_sigma * sqrt(inter)))^2), so the product's
+    entries have standard deviation about out_sigma; probs ~ U(0, 1). Draw kinds: 10 expert
+    counts, 15 h chunks, 16 one w_down slice per expert, 17 probs."""
+    name: str
+    tokens: int
+    inter: int
+    hidden: int
+    experts: int
+    seed: int
+    out_dtype: str = "bf16"       # "bf16" | "f32"
+    h_sigma: float = 0.5
+    out_sigma: float = 1.0
+    split: str = "dirichlet"
+
+    def flops(self) -> int:
+        return 2 * self.tokens * self.inter * self.hidden
+
+    def min_bytes(self) -> int:
+        """h, w_down, probs and offs read once, out written once."""
+        t, i, h, e = self.tokens, self.inter, self.hidden, self.experts
+        return t * i * 2 + e * h * i * 2 + 4 * t + 4 * e + t * h * ELEM_BYTES[self.out_dtype]
+
+    def counts(self) -> np.ndarray:
+        return expert_counts(self.seed, self.tokens, self.experts, self.split)
+
+    def offs(self) -> np.ndarray:
+        return np.cumsum(self.counts()).astype(np.int32)
+
+    def generate(self, threads: int | None = None) -> dict:
+        """h [tokens, inter], w_down [experts, hidden, inter] (bf16 bits), offs int32, probs float32."""
+        t, i, hd, e = self.tokens, self.inter, self.hidden, self.experts
+        w_sigma = np.float32(self.out_sigma / (self.h_sigma * np.sqrt(i)))
+        h = np.empty((t, i), dtype=np.uint16)
+        w = np.empty((e, hd, i), dtype=np.uint16)
+
+        def rng(kind: int, chunk: int) -> np.random.Generator:
+            return np.random.Generator(np.random.PCG64(np.random.SeedSequence(self.seed, spawn_key=(kind, chunk))))
+
+        def fill_h(chunk: int) -> None:
+            r0 = chunk * CHUNK_ROWS
+            m = min(CHUNK_ROWS, t - r0)
+            f = rng(15, chunk).standard_normal((m, i), dtype=np.float32)
+            f *= np.float32(self.h_sigma)
+            h[r0:r0 + m] = _to_bf16_bits(f)
+
+        def fill_w(ex: int) -> None:
+            f = rng(16, ex).standard_normal((hd, i), dtype=np.float32)
+            f *= w_sigma
+            w[ex] = _to_bf16_bits(f)
+
+        workers = threads or max(1, min(16, os.cpu_count() or 1))
+        with ThreadPoolExecutor(workers) as pool:
+            list(pool.map(fill_h, range((t + CHUNK_ROWS - 1) // CHUNK_ROWS)))
+            list(pool.map(fill_w, range(e)))
+        probs = rng(17, 0).random(t, dtype=np.float32)
+        return {"h": h, "w_down": w, "offs": self.offs(), "probs": probs}
+
+
+@dataclass(frozen=True)
+class CombineWorkload:
+    """Combine of routed rows into tokens on one expert-parallel rank.
+
+    Each token routes to top_k distinct experts out of global_experts, uniformly at random (slot
+    j holds the j-th pick); this rank holds experts [0, local_experts). The slots routed here
+    are numbered as the permuted rows are laid out, grouped by local expert and in token order
+    inside each expert; row_of[t, j] is that row, or -1 for a slot of another rank's expert.
+    expert_out ~ N(0, sigma^2) rows (the router-weighted expert outputs) of eo_dtype. Draw
+    kinds: 18 routing (per chunk of tokens), 19 expert_out (per chunk of rows)."""
+    name: str
+    tokens: int
+    hidden: int
+    top_k: int
+    global_experts: int
+    local_experts: int
+    seed: int
+    eo_dtype: str = "f32"
+    sigma: float = 0.05
+
+    def _rng(self, kind: int, chunk: int) -> np.random.Generator:
+        return np.random.Generator(np.random.PCG64(np.random.SeedSequence(self.seed, spawn_key=(kind, chunk))))
+
+    def routing(self) -> np.ndarray:
+        """int32 [tokens, top_k]: the expert of each slot (distinct within a token)."""
+        t, k, ge = self.tokens, self.top_k, self.global_experts
+        out = np.empty((t, k), dtype=np.int32)
+        for chunk in range((t + CHUNK_ROWS - 1) // CHUNK_ROWS):
+            r0 = chunk * CHUNK_ROWS
+            m = min(CHUNK_ROWS, t - r0)
+            keys = self._rng(18, chunk).random((m, ge))
+            out[r0:r0 + m] = np.argsort(keys, axis=1, kind="stable")[:, :k]
+        return out
+
+    def row_of(self, experts: np.ndarray | None = None) -> tuple[np.ndarray, int]:
+        """(row_of int32 [tokens, top_k], rows): local slots numbered by (expert, token)."""
+        ex = self.routing() if experts is None else experts
+        local = ex < self.local_experts
+        t_idx, j_idx = np.nonzero(local)
+        order = np.lexsort((t_idx, ex[t_idx, j_idx]))           # by expert, then token
+        row_of = np.full(ex.shape, -1, dtype=np.int32)
+        row_of[t_idx[order], j_idx[order]] = np.arange(order.size, dtype=np.int32)
+        return row_of, int(order.size)
+
+    def min_bytes(self, row_of: np.ndarray, rows: int) -> int:
+        """Each local slot's row read once, row_of read once, out written once."""
+        valid = int(((row_of >= 0) & (row_of < rows)).sum())
+        return valid * self.hidden * ELEM_BYTES[self.eo_dtype] + row_of.size * 4 + self.tokens * self.hidden * 4
+
+    def generate(self, threads: int | None = None) -> dict:
+        """expert_out [rows, hidden] (bf16/f16 bits as uint16 for 16-bit dtypes, float32 otherwise),
+        row_of int32 [tokens, top_k], rows."""
+        row_of, rows = self.row_of()
+        hd = self.hidden
+        dt = np.float32 if self.eo_dtype == "f32" else np.uint16
+        eo = np.empty((rows, hd), dtype=dt)
+
+        def fill(chunk: int) -> None:
+            r0 = chunk * CHUNK_ROWS
+            m = min(CHUNK_ROWS, rows - r0)
+            f = self._rng(19, chunk).standard_normal((m, hd), dtype=np.float32)
+            f *= np.float32(self.sigma)
+            if self.eo_dtype == "f32":
+                eo[r0:r0 + m] = f
+            elif self.eo_dtype == "bf16":
+                eo[r0:r0 + m] = _to_bf16_bits(f)
+            else:
+                eo[r0:r0 + m] = f.astype(np.float16).view(np.uint16)
+
+        workers = threads or max(1, min(16, os.cpu_count() or 1))
+        with ThreadPoolExecutor(workers) as pool:
+            list(pool.map(fill, range((rows + CHUNK_ROWS - 1) // CHUNK_ROWS)))
+        return {"expert_out": eo, "row_of": row_of, "rows": rows}
+
+
+DOWN_WORKLOADS = {
+    w.name: w for w in [
+        DownWorkload("down_4096x512x1024_e5", 4096, 512, 1024, 5, seed=22, split="one_empty"),
+        DownWorkload("down_4096x512x1024_e5_f32", 4096, 512, 1024, 5, seed=23, out_dtype="f32"),
+        DownWorkload("down_131072x2048x7168_e8", 131072, 2048, 7168, 8, seed=24),
+        DownWorkload("down_131072x2048x7168_e8_f32", 131072, 2048, 7168, 8, seed=25, out_dtype="f32"),
+    ]
+}
+
+COMBINE_WORKLOADS = {
+    w.name: w for w in [
+        CombineWorkload("combine_4096x1024_k8_e64of8", 4096, 1024, 8, 64, 8, seed=26),
+        CombineWorkload("combine_131072x7168_k8_e64of8", 131072, 7168, 8, 64, 8, seed=27),
+    ]
+}
 
 GROUPED_WORKLOADS = {
     w.name: w for w in [

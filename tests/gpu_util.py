@@ -147,3 +147,65 @@ def assert_gemm_bf16_within(got_bits: np.ndarray, exact: np.ndarray, abs_sum: np
     from tests.numerics import f64_to_bf16_exact
     return {"n": int(got.size), "equal_to_exact_rounding": float((got_bits == f64_to_bf16_exact(exact)).mean()),
             "max_err_over_bound": float((err / bound).max(initial=0))}
+
+
+# ---- down projection + router multiply ------------------------------------------
+#
+# out = round_out(fp32(c) * p) where c is the kernel's bf16 GEMM output. c itself
+# is not an output, so the bar asks that some bf16 value c that passes the GEMM
+# bound above (|c - S| <= 2 gamma_K sum|h*w| + half a bf16 ulp) gives exactly
+# `got` through the router multiply's definition: one binary32 product, rounded
+# once to the output dtype. For float32 output c is the bf16 value nearest to
+# got / p (the product's own rounding, 2^-24 relative, is far below bf16's
+# spacing); for bf16 output the candidates are the bf16 values within 3 ulps of
+# got / p, and -0. The bf16 rounding of the exact sum is tried first in both.
+
+def _bf16_from_order(o: np.ndarray) -> np.ndarray:
+    o = np.asarray(o, dtype=np.int64)
+    return np.where(o >= 0, o, 0x8000 | (-o)).astype(np.uint16)
+
+
+def assert_down_router_within(got: np.ndarray, out_is_f32: bool, exact: np.ndarray, abs_sum: np.ndarray,
+                              probs: np.ndarray, k: int, what: str) -> dict:
+    from tests.numerics import bf16_bits_to_f32, bf16_order, f64_to_bf16_exact
+    u = 2.0 ** -24
+    gamma = k * u / (1 - k * u)
+    p = np.broadcast_to(np.asarray(probs, np.float32).reshape(-1, 1), exact.shape)
+    got_f = got.astype(np.float64) if out_is_f32 else bf16_to_f64(got)
+    zero_p = p == 0
+    assert (got_f[zero_p] == 0).all(), f"{what}: nonzero output where the probability is 0"
+    nz = ~zero_p
+    ratio = np.where(nz, got_f / np.where(nz, p, 1).astype(np.float64), 0.0)
+    center = bf16_order(f64_to_bf16_exact(ratio))
+
+    def bound_ok(c_bits):
+        c = bf16_bits_to_f32(c_bits).astype(np.float64)
+        bound = 2 * gamma * abs_sum + 0.5 * bf16_spacing(np.maximum(np.abs(c), np.abs(exact)))
+        return np.abs(c - exact) <= bound
+
+    def through_router(c_bits):
+        prod = bf16_bits_to_f32(c_bits) * p                     # one binary32 product
+        return prod if out_is_f32 else f64_to_bf16_exact(prod.astype(np.float64))
+
+    ok = zero_p.copy()
+    chosen = np.zeros(exact.shape, np.uint16)
+    steps = [0] if out_is_f32 else [0, -1, 1, -2, 2, -3, 3]
+    # the exact sum's own rounding first, so the statistic below counts the outputs it explains
+    cands = [f64_to_bf16_exact(exact)] + [_bf16_from_order(center + s) for s in steps] + \
+        [np.full(exact.shape, 0x8000, np.uint16)]
+    for c in cands:
+        r = through_router(c)
+        same = (r.view(np.uint32) == got.view(np.uint32)) if out_is_f32 else (r == got)
+        hit = ~ok & same & bound_ok(c)
+        chosen[hit] = c[hit]
+        ok |= hit
+    bad = ~ok
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {got.size} outputs are not the router multiply of a bf16 "
+                           f"value within the fp32-accumulation bound (first at {np.argmax(bad.ravel())})")
+    eq = chosen[nz] == f64_to_bf16_exact(exact[nz])
+    return {"n": int(got.size), "c_equal_to_exact_rounding": float(eq.mean()) if eq.size else 1.0}
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    from tests.numerics import bf16_bits_to_f32
+    return bf16_bits_to_f32(bits).astype(np.float64)

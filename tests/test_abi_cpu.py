@@ -200,3 +200,58 @@ def test_grouped_binding_rejects_bad_tensors():
         binding.grouped_gate_up_swiglu_fwd(a, w, w, offs, p, y, None, 7.0)
     with pytest.raises(ValueError):                    # 2-D weights
         binding.grouped_gate_up_swiglu_fwd(a, w[0], w[0], offs, p, y, None, 7.0)
+
+
+# ---- down projection + router multiply, and the combine ----------------------------
+
+def dn(L, h=A, w=B, offs=D, p=E, out=F, odt=0, tokens=256, inter=64, hidden=32, experts=4):
+    return L.grouped_down_router_fwd(h, w, offs, p, out, odt, tokens, inter, hidden, experts, None)
+
+
+def test_down_validation(L):
+    for kw in ({"h": None}, {"w": None}, {"offs": None}, {"p": None}, {"out": None}):
+        assert dn(L, **kw) == NULLP, kw
+    for kw in ({"tokens": -1}, {"inter": 0}, {"hidden": 0}, {"experts": 0}, {"inter": 60}, {"hidden": 36},
+               {"tokens": 2 ** 31}, {"experts": 2 ** 62, "hidden": 8}):
+        assert dn(L, **kw) == SHAPE, kw
+    for odt in (1, 3, -1):                             # float16 output is not offered
+        assert dn(L, odt=odt) == DTYPE, odt
+    assert dn(L, tokens=0) == OK and dn(L, tokens=0, h=None) == OK
+    for kw in ({"h": A + 2}, {"w": B + 8}, {"out": F + 4}, {"offs": D + 2}, {"p": E + 1}):
+        assert dn(L, **kw) == MISAL, kw
+    for kw in ({"out": A}, {"out": B}, {"out": D}, {"out": E - 16}):
+        assert dn(L, **kw) == ALIAS, kw
+    assert dn(L, out=E - 16, odt=2) == ALIAS           # fp32 output: twice the bytes
+
+
+def cb(L, eo=A, edt=2, ro=B, out=C, rows=100, tokens=64, top_k=8, hidden=16):
+    return L.moe_combine_fwd(eo, edt, ro, out, rows, tokens, top_k, hidden, None)
+
+
+def test_combine_validation(L):
+    for kw in ({"eo": None}, {"ro": None}, {"out": None}):
+        assert cb(L, **kw) == NULLP, kw
+    for kw in ({"rows": -1}, {"tokens": -1}, {"top_k": 0}, {"top_k": 1025}, {"hidden": 0}, {"hidden": 12},
+               {"hidden": 2 ** 29}, {"tokens": 2 ** 60, "top_k": 8}):
+        assert cb(L, **kw) == SHAPE, kw
+    for edt in (3, -1):
+        assert cb(L, edt=edt) == DTYPE, edt
+    assert cb(L, tokens=0) == OK
+    for kw in ({"eo": A + 8}, {"out": C + 4}, {"ro": B + 2}):
+        assert cb(L, **kw) == MISAL, kw
+    for kw in ({"out": A}, {"out": B}, {"out": A + 100 * 16 * 4 - 16}):
+        assert cb(L, **kw) == ALIAS, kw
+
+
+def test_down_and_combine_bindings_reject_cpu_tensors():
+    h = torch.zeros(16, 64, dtype=torch.bfloat16)
+    w = torch.zeros(2, 32, 64, dtype=torch.bfloat16)
+    offs = torch.tensor([8, 16], dtype=torch.int32)
+    p = torch.zeros(16)
+    out = torch.zeros(16, 32, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        binding.grouped_down_router_fwd(h, w, offs, p, out)
+    eo = torch.zeros(10, 32)
+    ro = torch.zeros(16, 4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        binding.moe_combine_fwd(eo, ro, out)

@@ -1,0 +1,269 @@
+"""GPU parity of the down-projection grouped GEMM with the router-weight multiply
+(grouped_down_router_fwd) and of the combine of routed rows into tokens
+(moe_combine_fwd), against the oracle.
+
+Bars (tests/gpu_util.py):
+  - down: every output is the router multiply (one binary32 product, rounded
+    once to the output dtype) of a bf16 value within the fp32-accumulation bound
+    of the exact grouped sum; the bf16 output is, bit for bit, the bf16 rounding
+    of the float32 output (the same GEMM, one more rounding); rows of no expert
+    are left untouched;
+  - combine: bit-exact (the same binary32 additions in the same order).
+The exact grouped sums and their absolute sums come from the oracle's grouped
+product (oracle.grouped_gate_up with the down weights as both operands: the
+same grouped definition with the roles of the widths swapped).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_routed_expert_amd as epi
+import oracle
+from moe_routed_expert_amd.workloads import (COMBINE_WORKLOADS, DOWN_WORKLOADS, CombineWorkload, DownWorkload)
+from tests.gpu_util import assert_down_router_within, to_dev_bf16, to_host_bits
+
+pytestmark = pytest.mark.gpu
+SENTINEL16 = 0x7FBF          # a bf16 NaN pattern the kernel never writes
+SENTINEL32 = 0x7FC0DEAD      # a float32 NaN pattern the kernel never writes
+
+
+def say(msg):
+    print(f"\n[gpu-down-combine] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    epi.binding.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def covered_rows(offs, tokens):
+    cov = np.zeros(tokens, bool)
+    start = 0
+    for c in offs:
+        end = min(max(int(c), start), tokens)
+        cov[start:end] = True
+        start = end
+    return cov
+
+
+# ---- down projection ------------------------------------------------------------
+
+def run_down(d, tokens, hidden, f32):
+    h, w = to_dev_bf16(d["h"]), to_dev_bf16(d["w_down"])
+    offs = torch.from_numpy(d["offs"]).cuda()
+    p = torch.from_numpy(d["probs"]).cuda()
+    if f32:
+        out = torch.full((tokens, hidden), SENTINEL32, dtype=torch.int32, device="cuda").view(torch.float32)
+    else:
+        out = torch.full((tokens, hidden), SENTINEL16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    epi.grouped_down_router_fwd(h, w, offs, p, out)
+    return out
+
+
+def exact_sums(h, w_down, offs, tokens, inter, hidden, experts):
+    s, s_abs = oracle.grouped_gate_up(h, w_down, w_down, offs, tokens, inter, hidden, experts, with_abs_sum=True)
+    return s[:, :hidden], s_abs[:, :hidden]
+
+
+def check_down(d, tokens, inter, hidden, experts, what):
+    o32 = run_down(d, tokens, hidden, True)
+    o16 = run_down(d, tokens, hidden, False)
+    torch.cuda.synchronize()
+    g32 = o32.cpu().numpy()
+    g16 = to_host_bits(o16)
+    cov = covered_rows(d["offs"], tokens)
+    assert (g32[~cov].view(np.uint32) == SENTINEL32).all(), f"{what}: fp32 rows of no expert written"
+    assert (g16[~cov] == SENTINEL16).all(), f"{what}: bf16 rows of no expert written"
+    want16 = torch.from_numpy(np.ascontiguousarray(g32[cov])).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(g16[cov], want16.view(np.uint16)), f"{what}: bf16 output is not bf16(fp32 output)"
+    s, s_abs = exact_sums(d["h"], d["w_down"], d["offs"], tokens, inter, hidden, experts)
+    p = d["probs"][cov]
+    st32 = assert_down_router_within(g32[cov], True, s[cov], s_abs[cov], p, inter, f"{what} fp32")
+    st16 = assert_down_router_within(g16[cov], False, s[cov], s_abs[cov], p, inter, f"{what} bf16")
+    say(f"{what}: fp32 {st32}, bf16 {st16}")
+
+
+@pytest.mark.parametrize("name", ["down_4096x512x1024_e5", "down_4096x512x1024_e5_f32"])
+def test_small_named_workloads(name):
+    w = DOWN_WORKLOADS[name]
+    check_down(w.generate(), w.tokens, w.inter, w.hidden, w.experts, w.name)
+
+
+# tails: tokens not a multiple of 256 per expert; inter not a multiple of 64 (a
+# partial K step); hidden not a multiple of 256 (the block's second 128-column
+# tile partial, or absent: hidden 120 and 376); one expert; many small experts
+@pytest.mark.parametrize("tokens,inter,hidden,experts,split", [
+    (300, 64, 256, 3, "dirichlet"), (257, 200, 136, 4, "one_empty"), (1000, 256, 512, 1, "even"),
+    (129, 96, 120, 7, "dirichlet"), (640, 1032, 376, 16, "dirichlet"), (1, 8, 8, 1, "even"),
+    (513, 2048, 264, 2, "dirichlet"),
+])
+def test_down_shapes(tokens, inter, hidden, experts, split):
+    w = DownWorkload(f"d_{tokens}x{inter}x{hidden}_e{experts}", tokens, inter, hidden, experts,
+                     seed=tokens + inter + hidden + experts, split=split)
+    check_down(w.generate(), tokens, inter, hidden, experts, w.name)
+
+
+@pytest.mark.parametrize("offs", [[50, 20, 300, 100], [0, 0, 0, 257], [257, 257, 257, 257], [-5, 10, 10, 200],
+                                  [100, 1000, 5, 7]])
+def test_down_counts_that_are_empty_decreasing_or_too_large(offs):
+    w = DownWorkload("d_offs", 257, 64, 40, 4, seed=32)
+    d = w.generate()
+    d["offs"] = np.array(offs, dtype=np.int32)
+    check_down(d, 257, 64, 40, 4, f"offs {offs}")
+
+
+def test_down_zero_probabilities_and_zero_rows():
+    w = DownWorkload("d_zeros", 384, 128, 264, 3, seed=33)
+    d = w.generate()
+    d["probs"][::7] = 0.0
+    d["h"][5::11] = 0x8000                    # rows of -0: every product is +-0, the sum +0
+    check_down(d, 384, 128, 264, 3, "zero probs / zero rows")
+
+
+@pytest.mark.parametrize("name", ["down_131072x2048x7168_e8", "down_131072x2048x7168_e8_f32"])
+def test_down_full_size_sampled_rows(name):
+    w = DOWN_WORKLOADS[name]
+    f32 = w.out_dtype == "f32"
+    say(f"{w.name}: generate")
+    d = w.generate()
+    say(f"{w.name}: gpu")
+    out = run_down(d, w.tokens, w.hidden, f32)
+    offs = d["offs"].astype(np.int64)
+    starts = np.concatenate([[0], offs[:-1]])
+    rng = np.random.default_rng(6)
+    pick = set()
+    for s0, e0 in zip(starts, offs):
+        if e0 > s0:
+            pick |= {s0, s0 + 1, e0 - 1, min(s0 + 255, e0 - 1), min(s0 + 256, e0 - 1)}
+    pick |= set(rng.integers(0, w.tokens, 200).tolist())
+    idx = np.array(sorted(pick))
+    sub = out[torch.from_numpy(idx).cuda()]
+    torch.cuda.synchronize()
+    got = sub.cpu().numpy() if f32 else to_host_bits(sub)
+    if f32:
+        assert not (out.view(torch.int32) == SENTINEL32).any().item(), f"{w.name}: rows left unwritten"
+    else:
+        assert not (out.view(torch.int16) == SENTINEL16).any().item(), f"{w.name}: rows left unwritten"
+    expert_of = np.searchsorted(offs, idx, side="right")
+    sub_offs = np.array([np.sum(expert_of <= e) for e in range(w.experts)], dtype=np.int32)
+    say(f"{w.name}: oracle on {idx.size} sampled rows")
+    s, s_abs = exact_sums(d["h"][idx], d["w_down"], sub_offs, idx.size, w.inter, w.hidden, w.experts)
+    st = assert_down_router_within(got, f32, s, s_abs, d["probs"][idx], w.inter, w.name)
+    say(f"{w.name}: {st}")
+
+
+# ---- combine ------------------------------------------------------------------------
+
+EO_TORCH = {oracle.BF16: torch.bfloat16, oracle.F16: torch.float16, oracle.F32: torch.float32}
+EO_CODE = {"bf16": oracle.BF16, "f16": oracle.F16, "f32": oracle.F32}
+
+
+def eo_to_dev(eo, code):
+    if code == oracle.F32:
+        return torch.from_numpy(np.ascontiguousarray(eo, np.float32)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(eo).view(np.int16)).view(EO_TORCH[code]).cuda()
+
+
+def eo_for_oracle(eo, code):
+    return eo.view(np.float16) if code == oracle.F16 else eo
+
+
+def run_combine(eo, code, row_of, hidden):
+    tokens = row_of.shape[0]
+    out = torch.full((tokens, hidden), SENTINEL32, dtype=torch.int32, device="cuda").view(torch.float32)
+    epi.moe_combine_fwd(eo_to_dev(eo, code), torch.from_numpy(np.ascontiguousarray(row_of)).cuda(), out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check_combine(eo, code, row_of, rows, hidden, what):
+    tokens, top_k = row_of.shape
+    got = run_combine(eo, code, row_of, hidden)
+    want = oracle.moe_combine(eo_for_oracle(eo, code), code, row_of, rows, tokens, top_k, hidden)
+    nan_w, nan_g = np.isnan(want), np.isnan(got)
+    assert np.array_equal(nan_w, nan_g), f"{what}: NaN positions differ"
+    bad = ~nan_w & (got.view(np.uint32) != want.view(np.uint32))
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {got.size} differ (bit-exact bar)"
+    say(f"{what}: {got.size} bit-exact")
+
+
+def test_combine_small_named_workload():
+    w = COMBINE_WORKLOADS["combine_4096x1024_k8_e64of8"]
+    d = w.generate()
+    check_combine(d["expert_out"], EO_CODE[w.eo_dtype], d["row_of"], d["rows"], w.hidden, w.name)
+
+
+# hidden: one quad per lane or fewer (8, 520), several (1032: two, 7168: seven),
+# more than one pass over the row (8200: nine quads per lane, capped at eight)
+@pytest.mark.parametrize("eo_dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("tokens,hidden,top_k,ge,le", [
+    (777, 1032, 8, 64, 8), (300, 8, 2, 8, 4), (513, 520, 4, 16, 16), (64, 8200, 6, 32, 32), (1, 7168, 1, 4, 2),
+])
+def test_combine_shapes_and_dtypes(eo_dtype, tokens, hidden, top_k, ge, le):
+    w = CombineWorkload(f"c_{tokens}x{hidden}_k{top_k}_e{ge}of{le}_{eo_dtype}", tokens, hidden, top_k, ge, le,
+                        seed=tokens + hidden + top_k, eo_dtype=eo_dtype, sigma=3.0)
+    d = w.generate()
+    check_combine(d["expert_out"], EO_CODE[eo_dtype], d["row_of"], d["rows"], hidden, w.name)
+
+
+def test_combine_signed_zeros_infinities_and_odd_slots():
+    """-0 rows (a token whose only rows are -0 gets +0), infinities (inf - inf is NaN),
+    order-sensitive magnitudes, duplicated rows, and slot indices that are negative or
+    past the last row."""
+    rng = np.random.default_rng(40)
+    rows, tokens, top_k, hidden = 12, 40, 5, 16
+    eo = rng.standard_normal((rows, hidden)).astype(np.float32)
+    eo[0] = -0.0
+    eo[1, :4] = np.inf
+    eo[2, :4] = -np.inf
+    eo[3] = 2.0 ** 24
+    eo[4] = 1.0
+    row_of = rng.integers(-3, rows + 4, (tokens, top_k)).astype(np.int32)
+    row_of[0] = [0, 0, -1, 99, 0]
+    row_of[1] = [1, 2, 3, 4, 4]
+    row_of[2] = [3, 4, 4, -7, 12]
+    row_of[3] = [4, 4, 3, 0, 1]
+    row_of[4] = [-1, -1, -1, -1, -1]
+    check_combine(eo, oracle.F32, row_of, rows, hidden, "zeros / infinities / odd slots")
+    got = run_combine(eo, oracle.F32, row_of, hidden)
+    assert (got[0] == 0).all() and not np.signbit(got[0]).any()
+    assert (got[4] == 0).all() and not np.signbit(got[4]).any()
+
+
+def test_combine_no_local_rows():
+    """rows == 0: every slot is another rank's; out is +0 everywhere (expert_out is empty)."""
+    tokens, top_k, hidden = 33, 3, 24
+    out = torch.full((tokens, hidden), 7.0, dtype=torch.float32, device="cuda")
+    eo = torch.empty((0, hidden), dtype=torch.float32, device="cuda")
+    row_of = torch.from_numpy(np.arange(tokens * top_k, dtype=np.int32).reshape(tokens, top_k) % 5 - 2).cuda()
+    epi.moe_combine_fwd(eo, row_of, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert (got == 0).all() and not np.signbit(got).any()
+
+
+def test_combine_full_size_sampled_tokens():
+    w = COMBINE_WORKLOADS["combine_131072x7168_k8_e64of8"]
+    say(f"{w.name}: generate")
+    d = w.generate()
+    code, row_of, rows = EO_CODE[w.eo_dtype], d["row_of"], d["rows"]
+    say(f"{w.name}: gpu ({rows} rows)")
+    out = torch.full((w.tokens, w.hidden), SENTINEL32, dtype=torch.int32,
+                     device="cuda").view(torch.float32)
+    epi.moe_combine_fwd(eo_to_dev(d["expert_out"], code), torch.from_numpy(row_of).cuda(), out)
+    assert not (out.view(torch.int32) == SENTINEL32).any().item(), f"{w.name}: elements left unwritten"
+    rng = np.random.default_rng(7)
+    n_local = (row_of >= 0).sum(1)
+    idx = np.unique(np.concatenate([rng.integers(0, w.tokens, 300), np.flatnonzero(n_local >= 3)[:20],
+                                    np.flatnonzero(n_local == 0)[:20], [0, w.tokens - 1]]))
+    got = out[torch.from_numpy(idx).cuda()].cpu().numpy()
+    want = oracle.moe_combine(d["expert_out"], code, row_of[idx], rows, idx.size, w.top_k, w.hidden)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"{w.name}: sampled tokens differ"
+    say(f"{w.name}: {idx.size} sampled tokens bit-exact")

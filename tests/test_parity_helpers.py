@@ -56,3 +56,63 @@ def test_bf16_bar_exact_mode_and_zero_sign():
         assert_bf16_parity(np.array([one]), np.array([next_one]), "exact", exact=True)
     with pytest.raises(AssertionError, match="sign of a zero"):
         assert_bf16_parity(np.array([0x0000], np.uint16), np.array([0x8000], np.uint16), "zero")
+
+
+# ---- the down-projection bar -----------------------------------------------------
+
+def _down_case(out_dtype):
+    import oracle
+    from moe_routed_expert_amd.workloads import DownWorkload
+    w = DownWorkload("helper", 300, 64, 40, 3, seed=50, out_dtype="f32" if out_dtype == oracle.F32 else "bf16")
+    d = w.generate()
+    d["probs"][::9] = 0.0
+    out = oracle.grouped_down_router_fwd(d["h"], d["w_down"], d["offs"], d["probs"], w.tokens, w.inter, w.hidden,
+                                         w.experts, out_dtype=out_dtype)
+    s, s_abs = oracle.grouped_gate_up(d["h"], d["w_down"], d["w_down"], d["offs"], w.tokens, w.inter, w.hidden,
+                                      w.experts, with_abs_sum=True)
+    return out, s[:, :w.hidden], s_abs[:, :w.hidden], d["probs"], w.inter
+
+
+@pytest.mark.parametrize("f32", [True, False])
+def test_down_bar_accepts_the_oracle_and_finds_its_rounding(f32):
+    import oracle
+    from tests.gpu_util import assert_down_router_within
+    out, s, s_abs, p, k = _down_case(oracle.F32 if f32 else oracle.BF16)
+    st = assert_down_router_within(out, f32, s, s_abs, p, k, "oracle")
+    assert st["c_equal_to_exact_rounding"] == 1.0
+
+
+def test_down_bar_rejects_one_float32_ulp():
+    import oracle
+    from tests.gpu_util import assert_down_router_within
+    out, s, s_abs, p, k = _down_case(oracle.F32)
+    bad = out.copy()
+    i = np.flatnonzero((p != 0) & (np.abs(out[:, 0]) > 0))[3]
+    bad[i, 0] = np.nextafter(bad[i, 0], np.float32(np.inf))
+    with pytest.raises(AssertionError, match="not the router multiply"):
+        assert_down_router_within(bad, True, s, s_abs, p, k, "planted")
+
+
+@pytest.mark.parametrize("f32", [True, False])
+def test_down_bar_rejects_a_value_off_by_a_few_bf16_ulps(f32):
+    import oracle
+    from tests.gpu_util import assert_down_router_within
+    out, s, s_abs, p, k = _down_case(oracle.F32 if f32 else oracle.BF16)
+    bad = out.copy()
+    i = np.flatnonzero((p != 0) & (np.abs(s[:, 1]) > 0.5))[2]
+    if f32:
+        bad[i, 1] = np.float32(bad[i, 1] * np.float32(1 + 2.0 ** -5))
+    else:
+        bad[i, 1] = bad[i, 1] + 6                      # 6 bf16 ulps up (same sign, no binade edge near 0.5)
+    with pytest.raises(AssertionError, match="not the router multiply"):
+        assert_down_router_within(bad, f32, s, s_abs, p, k, "planted")
+
+
+def test_down_bar_rejects_a_nonzero_output_where_the_probability_is_zero():
+    import oracle
+    from tests.gpu_util import assert_down_router_within
+    out, s, s_abs, p, k = _down_case(oracle.F32)
+    bad = out.copy()
+    bad[0, 0] = 1e-30                                  # p[0] == 0
+    with pytest.raises(AssertionError, match="probability is 0"):
+        assert_down_router_within(bad, True, s, s_abs, p, k, "planted")
