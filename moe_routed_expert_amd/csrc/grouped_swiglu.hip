@@ -32,9 +32,11 @@
 //     padded (a wavefront's load fills 1 KiB contiguously); an XOR swizzle of
 //     each row's 16-byte chunks keeps the fragment reads conflict-free.
 //   * Within a K step, the next 16-wide sub-step's fragments are read from LDS
-//     while the current one's MFMAs run. One barrier per K step, a bare
-//     s_barrier after explicit waits (a __syncthreads() fence would also wait
-//     for the loads still in flight).
+//     while the current one's MFMAs run, one read placed after each MFMA. One
+//     barrier per K step, before the last sub-step, a bare s_barrier after
+//     explicit waits (a __syncthreads() fence would also wait for the loads
+//     still in flight); the loads of the step after next and the next step's
+//     first fragments are issued while the last sub-step's MFMAs run.
 //   * Tiles never straddle experts: each block finds its expert and row range
 //     from offs on the device (no host copy of offs), so a grid sized for
 //     the worst case, ceil(tokens / 256) + experts row tiles, covers any split.
@@ -49,10 +51,14 @@
 // Measured at 131072 x 7168 x 2048 with 8 experts (every configuration gives
 // bit-identical results, each output being accumulated in the same order):
 // register-staged loads with padded LDS ran at 746-918 TFLOP/s over 22 tile
-// shapes, deeper load pipelines and fragment pipelining at up to 953, and this
-// configuration at 965 (988 without x_out). Hardware counters put LDS bank
-// conflicts at 0.5% of LDS cycles and show the wavefronts waiting about half
-// their cycles (loads and barriers of a single resident block).
+// shapes, deeper load pipelines and fragment pipelining at up to 953, the
+// same tiles with one barrier per step at 941-965, and this loop at 1040-1060
+// (MFMA busy 54% of cycles, LDS 21%, bank conflicts 0.8% of LDS cycles).
+// Variants that did not help: K steps of 32 with 3-5 stages (850-890), two
+// 128 x 128 blocks per CU (870-890), other read placements (1007-1049), a
+// branch-free unrolled loop (1022-1032), an L2 prefetch two to four steps
+// ahead (930). Timing with the in-loop loads removed gave 1430: waiting on
+// the loads of the next stage is the largest remaining cost.
 #include "epi_common.h"
 #include "swiglu_math.h"
 
@@ -153,12 +159,11 @@ int64_t grouped_grid(int64_t tokens, int64_t n_cols, int64_t cols_per_tile, int6
 // ---- the kernel -------------------------------------------------------------------
 //
 // Global loads write straight into LDS (global_load_lds_dwordx4: each lane's
-// 16 bytes land at the wavefront's LDS base + 16 * lane), S - 1 K steps ahead
-// through a ring of S LDS stages, no register staging. A wavefront's load
-// fills 1 KiB of LDS contiguously, so tiles are not padded: chunk kq of a row
-// (BK / 8 chunks of 16 bytes) is placed at slot row * (BK / 8) + (kq ^ swz(row)),
-// which keeps the 16-byte fragment reads conflict-free. Chunks outside the
-// matrices (row or K tails) are written as zeros with an ordinary LDS store.
+// 16 bytes land at the wavefront's LDS base + 16 * lane), one K step ahead
+// through two LDS stages, no register staging. A wavefront's load fills 1 KiB
+// of LDS contiguously, so tiles are not padded: chunk kq of a row (BK / 8
+// chunks of 16 bytes) is placed at slot row * (BK / 8) + (kq ^ swz(row)),
+// which keeps the 16-byte fragment reads conflict-free.
 template <int BM_, int BN_, int WM_, int WN_, int S_, int OCC_, int GM_ = 1, int BK_ = 32>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, S = S_, OCC = OCC_, GM = GM_;
@@ -173,12 +178,11 @@ struct Cfg {
     static constexpr int kLdo = BN + 8;
     static constexpr int kAChunks = BM * BK / 8 / kThreads;
     static constexpr int kWChunks = BN * BK / 8 / kThreads;
-    static constexpr int kDmaPerStage = kAChunks + 2 * kWChunks;  // load instructions per thread per stage
     static constexpr int kLdsElems = S * kStageElems > BM * kLdo ? S * kStageElems : BM * kLdo;
     static_assert(MI >= 1 && NI >= 1 && BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "whole MFMA tiles");
     static_assert(kAChunks >= 1 && kWChunks >= 1 && BM * BK % (8 * kThreads) == 0 && BN * BK % (8 * kThreads) == 0,
                   "whole 16-byte chunks per thread");
-    static_assert(S >= 2 && (S - 2) * kDmaPerStage <= 63, "outstanding loads fit the vmcnt counter");
+    static_assert(S == 2, "two LDS stages");
     static_assert(BM * BN % (8 * kThreads) == 0, "whole output chunks per thread");
 };
 
@@ -199,29 +203,6 @@ __device__ __forceinline__ int swz(int row) {
 template <int kCpr>
 __device__ __forceinline__ int slot_of(int row, int kq) { return row * kCpr + (kq ^ swz<kCpr>(row)); }
 
-// Issue this thread's loads of one operand tile into `tile` (LDS): chunk i of
-// wavefront w covers slots [(i * threads + w * 64), +64), lane l slot + l.
-template <class C, int N>
-__device__ __forceinline__ void dma_tile(uint16_t* tile, const uint16_t* __restrict__ base, int64_t ld, int nrows,
-                                         int64_t k0, int64_t kend) {
-    const int lane = static_cast<int>(threadIdx.x) % 64;
-    const int wave = static_cast<int>(threadIdx.x) / 64;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const int wave_slot0 = i * C::kThreads + wave * 64;  // uniform across the wavefront
-        const int slot = wave_slot0 + lane;
-        const int row = slot / C::kCpr;
-        const int kq = (slot % C::kCpr) ^ swz<C::kCpr>(row);
-        const int64_t k = k0 + kq * 8;
-        if (row < nrows && k < kend)
-            __builtin_amdgcn_global_load_lds(base + row * ld + k,
-                                             (__attribute__((address_space(3))) void*)(tile + wave_slot0 * 8), 16, 0,
-                                             0);
-        else
-            *reinterpret_cast<u32x4*>(tile + slot * 8) = u32x4{0u, 0u, 0u, 0u};
-    }
-}
-
 template <int kCpr>
 __device__ __forceinline__ bf16x8 frag_swz(const uint16_t* tile, int row, int kq) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + slot_of<kCpr>(row, kq) * 8));
@@ -233,6 +214,184 @@ __device__ __forceinline__ bf16x8 frag_swz(const uint16_t* tile, int row, int kq
 template <int N>
 __device__ __forceinline__ void wait_loads_but() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// ---- the pipelined main loop ------------------------------------------------
+//
+// Two LDS stages of BK = 64 (four 16-wide sub-steps). Per K step the
+// wavefront runs sub-steps 0-2 with the next sub-step's fragments read while
+// the current sub-step's MFMAs run; then it waits for its own loads of the
+// next stage and for its last fragment reads of this stage, and the block
+// meets at one barrier. After it, nobody reads this stage any more and the
+// next stage is complete, so the loads of the stage after next go into this
+// stage's buffer and the next stage's first fragments are read, both while
+// sub-step 3's MFMAs run. Only the next stage's loads are in flight at the
+// barrier, so the wait is simply for all of them.
+//
+// Loads are issued without row bounds branches: a lane whose row lies past the
+// tile's valid rows loads the last valid row instead (its results are never
+// stored), so no load leaves the tensors, and the pointers are formed once per
+// tile. Only a K step that crosses the end of K takes the other path, which
+// writes zeros to LDS for the chunks past it (k_dim is a multiple of 8, so a
+// chunk is wholly in or out).
+template <class C>
+struct PipeLoads {
+    static constexpr int kA = C::kAChunks, kW = C::kWChunks;
+    const uint16_t* pa[kA];
+    const uint16_t* pg[kW];
+    const uint16_t* pu[kW];
+    int oa[kA], ow[kW];  // wave-uniform LDS slot of the chunk's first lane (in 16-byte units)
+    int ka[kA], kw[kW];  // the lane's K offset within the step (elements)
+
+    __device__ __forceinline__ PipeLoads(const uint16_t* a_tile, const uint16_t* g_tile, const uint16_t* u_tile,
+                                         int arows, int grows, int urows, int64_t ld) {
+        const int lane = static_cast<int>(threadIdx.x) % 64;
+        const int wave = static_cast<int>(threadIdx.x) / 64;
+#pragma unroll
+        for (int i = 0; i < kA; ++i) {
+            const int slot0 = i * C::kThreads + wave * 64;
+            const int row = (slot0 + lane) / C::kCpr;
+            const int kq = ((slot0 + lane) % C::kCpr) ^ swz<C::kCpr>(row);
+            oa[i] = slot0;
+            ka[i] = kq * 8;
+            pa[i] = a_tile + static_cast<int64_t>(row < arows ? row : arows - 1) * ld + kq * 8;
+        }
+#pragma unroll
+        for (int i = 0; i < kW; ++i) {
+            const int slot0 = i * C::kThreads + wave * 64;
+            const int row = (slot0 + lane) / C::kCpr;
+            const int kq = ((slot0 + lane) % C::kCpr) ^ swz<C::kCpr>(row);
+            ow[i] = slot0;
+            kw[i] = kq * 8;
+            pg[i] = g_tile + static_cast<int64_t>(row < grows ? row : grows - 1) * ld + kq * 8;
+            pu[i] = u_tile + static_cast<int64_t>(row < urows ? row : urows - 1) * ld + kq * 8;
+        }
+    }
+
+    __device__ __forceinline__ static void load(const uint16_t* src, uint16_t* dst) {
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    }
+    __device__ __forceinline__ static void zero(uint16_t* dst) {
+        *reinterpret_cast<u32x4*>(dst) = u32x4{0u, 0u, 0u, 0u};
+    }
+
+    // Loads of K step kt into `st` (one stage of LDS).
+    __device__ __forceinline__ void issue(uint16_t* st, int64_t kt, int64_t k_dim) const {
+        const int lane = static_cast<int>(threadIdx.x) % 64;
+        const int64_t k0 = kt * C::BK;
+        uint16_t* sa = st;
+        uint16_t* sg = st + C::kAElems;
+        uint16_t* su = st + C::kAElems + C::kWElems;
+        if (k0 + C::BK <= k_dim) {
+#pragma unroll
+            for (int i = 0; i < kA; ++i) load(pa[i] + k0, sa + oa[i] * 8);
+#pragma unroll
+            for (int i = 0; i < kW; ++i) {
+                load(pg[i] + k0, sg + ow[i] * 8);
+                load(pu[i] + k0, su + ow[i] * 8);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kA; ++i) {
+                if (k0 + ka[i] < k_dim)
+                    load(pa[i] + k0, sa + oa[i] * 8);
+                else
+                    zero(sa + (oa[i] + lane) * 8);
+            }
+#pragma unroll
+            for (int i = 0; i < kW; ++i) {
+                if (k0 + kw[i] < k_dim) {
+                    load(pg[i] + k0, sg + ow[i] * 8);
+                    load(pu[i] + k0, su + ow[i] * 8);
+                } else {
+                    zero(sg + (ow[i] + lane) * 8);
+                    zero(su + (ow[i] + lane) * 8);
+                }
+            }
+        }
+    }
+};
+
+template <class C>
+__device__ __forceinline__ void mainloop_pipe(uint16_t* lds, const uint16_t* a_tile, const uint16_t* g_tile,
+                                              const uint16_t* u_tile, int arows, int grows, int urows,
+                                              int64_t k_dim, f32x16 (&acc_g)[C::MI][C::NI],
+                                              f32x16 (&acc_u)[C::MI][C::NI]) {
+    constexpr int MI = C::MI, NI = C::NI, KK = C::BK / 16;
+    static_assert(C::S == 2 && KK >= 2, "two stages of at least two sub-steps");
+    const int lane = static_cast<int>(threadIdx.x) % 64;
+    const int wave = static_cast<int>(threadIdx.x) / 64;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const PipeLoads<C> ld(a_tile, g_tile, u_tile, arows, grows, urows, k_dim);
+    const int64_t nk = (k_dim + C::BK - 1) / C::BK;
+
+    bf16x8 fa[2][MI], fg[2][NI], fu[2][NI];
+    auto read = [&](const uint16_t* stage, int b, int kk) {
+        const uint16_t* sa = stage;
+        const uint16_t* sg = stage + C::kAElems;
+        const uint16_t* su = stage + C::kAElems + C::kWElems;
+        const int kq = kk * 2 + lane / 32;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+            fa[b][mi] = frag_swz<C::kCpr>(sa, wm * (C::BM / C::WM) + mi * 32 + lane % 32, kq);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+            fg[b][ni] = frag_swz<C::kCpr>(sg, wn * (C::BN / C::WN) + ni * 32 + lane % 32, kq);
+            fu[b][ni] = frag_swz<C::kCpr>(su, wn * (C::BN / C::WN) + ni * 32 + lane % 32, kq);
+        }
+    };
+    auto mfma = [&](int b) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) {
+                acc_g[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[b][mi], fg[b][ni], acc_g[mi][ni], 0, 0, 0);
+                acc_u[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[b][mi], fu[b][ni], acc_u[mi][ni], 0, 0, 0);
+            }
+    };
+    // one fragment read of the next sub-step after each of this sub-step's
+    // first MFMAs (left to itself, the compiler issued the reads after the
+    // MFMAs and waited for them at the start of every sub-step)
+    auto interleave = [&]() {
+        constexpr int kReads = MI + 2 * NI, kMfmas = 2 * MI * NI;
+#pragma unroll
+        for (int i = 0; i < kReads; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - kReads, 0);
+    };
+
+    ld.issue(lds, 0, k_dim);
+    wait_loads_but<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (nk > 1) ld.issue(lds + C::kStageElems, 1, k_dim);
+    read(lds, 0, 0);
+
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        uint16_t* cur = lds + (kt & 1) * C::kStageElems;
+        uint16_t* nxt = lds + ((kt + 1) & 1) * C::kStageElems;
+#pragma unroll
+        for (int kk = 0; kk + 1 < KK; ++kk) {
+            read(cur, (kk + 1) & 1, kk + 1);
+            mfma(kk & 1);
+            interleave();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kt + 1 < nk) {
+            // own loads of the next stage landed, own reads of this stage done; then the block meets
+            wait_loads_but<0>();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (kt + 2 < nk) ld.issue(cur, kt + 2, k_dim);
+            read(nxt, 0, 0);
+        }
+        mfma((KK - 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // Epilogues: the clamped SwiGLU of (gate, up) (two weight tensors, the same
@@ -285,72 +444,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
             acc_u[mi][ni] = f32x16{};
         }
 
-    const int64_t nk = (k_dim + C::BK - 1) / C::BK;
-    // Every wavefront issues exactly kDmaPerStage loads per stage only when no
-    // chunk of the tile lies outside the matrices (a wavefront whose chunk is
-    // out of range for all its lanes skips that load); otherwise the waits
-    // below fall back to waiting for every load.
-    const bool full = tr.rows == C::BM && ncols1 == C::BN && ncols2 == C::BN && k_dim % C::BK == 0;
-    auto issue = [&](int64_t kt) {
-        uint16_t* st = lds + (kt % S) * C::kStageElems;
-        const int64_t k0 = kt * C::BK;
-        dma_tile<C, C::kAChunks>(st, a_tile, k_dim, tr.rows, k0, k_dim);
-        dma_tile<C, C::kWChunks>(st + C::kAElems, g_tile, k_dim, ncols1, k0, k_dim);
-        dma_tile<C, C::kWChunks>(st + C::kAElems + C::kWElems, u_tile, k_dim, ncols2, k0, k_dim);
-    };
-#pragma unroll
-    for (int s = 0; s < S - 1; ++s)
-        if (s < nk) issue(s);
-
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        // this wavefront's loads of stage kt are done once at most the later
-        // stages' loads (kt + 1 .. kt + S - 2, those already issued) are pending
-        if (full && kt + S - 2 < nk)
-            wait_loads_but<(S - 2) * C::kDmaPerStage>();
-        else
-            wait_loads_but<0>();
-        // every wavefront's stage kt landed; stage kt - 1 is no longer read. A
-        // bare barrier: __syncthreads() would also wait for the later stages'
-        // loads still in flight (its fence covers every outstanding access).
-        // The empty asm statements keep the compiler from moving LDS accesses
-        // across the barrier (they emit no instruction).
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if (kt + S - 1 < nk) issue(kt + S - 1);
-        const uint16_t* cur = lds + (kt % S) * C::kStageElems;
-        const uint16_t* sa = cur;
-        const uint16_t* sg = cur + C::kAElems;
-        const uint16_t* su = cur + C::kAElems + C::kWElems;
-        // the next 16-wide K sub-step's fragments are read while this one's
-        // MFMAs run (two register sets)
-        constexpr int KK = C::BK / 16;
-        bf16x8 fa[2][MI], fg[2][NI], fu[2][NI];
-        auto read = [&](int b, int kk) {
-            const int kq = kk * 2 + lane / 32;
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-                fa[b][mi] = frag_swz<C::kCpr>(sa, wm * (C::BM / C::WM) + mi * 32 + lane % 32, kq);
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni) {
-                fg[b][ni] = frag_swz<C::kCpr>(sg, wn * (C::BN / C::WN) + ni * 32 + lane % 32, kq);
-                fu[b][ni] = frag_swz<C::kCpr>(su, wn * (C::BN / C::WN) + ni * 32 + lane % 32, kq);
-            }
-        };
-        read(0, 0);
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            if (kk + 1 < KK) read((kk + 1) & 1, kk + 1);
-            const int b = kk & 1;
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < NI; ++ni) {
-                    acc_g[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[b][mi], fg[b][ni], acc_g[mi][ni], 0, 0, 0);
-                    acc_u[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[b][mi], fu[b][ni], acc_u[mi][ni], 0, 0, 0);
-                }
-        }
-    }
+    mainloop_pipe<C>(lds, a_tile, g_tile, u_tile, tr.rows, ncols1, ncols2 > 0 ? ncols2 : 1, k_dim, acc_g, acc_u);
     __syncthreads();  // all fragment reads done before the buffers become the staging tile
 
     uint16_t* stage = lds;
