@@ -54,10 +54,11 @@
 // shapes, deeper load pipelines and fragment pipelining at up to 953, the
 // same tiles with one barrier per step at 941-965, and this loop at 1040-1060
 // (MFMA busy 54% of cycles, LDS 21%, bank conflicts 0.8% of LDS cycles).
-// Variants that did not help: K steps of 32 with 3-5 stages (850-890), two
+// Variants that did not help: K steps of 32 with 3-5 stages (850-912), two
 // 128 x 128 blocks per CU (870-890), other read placements (1007-1049), a
 // branch-free unrolled loop (1022-1032), an L2 prefetch two to four steps
-// ahead (930). Timing with the in-loop loads removed gave 1430: waiting on
+// ahead (930), A tiles three stages deep (929), four wavefronts of 128-row
+// tiles (950), raised wave priority around the MFMAs (997). Timing with the in-loop loads removed gave 1430: waiting on
 // the loads of the next stage is the largest remaining cost.
 #include "epi_common.h"
 #include "swiglu_math.h"
