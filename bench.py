@@ -48,6 +48,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -95,16 +96,25 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments removed and whitespace collapsed (string
+    literals in these sources hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest(op: str) -> str:
-    """Digest of one op's HIP sources and the build flags, to tell whether
-    counter readings taken earlier still describe the kernels being timed."""
+    """Digest of one op's HIP sources (code only, comments ignored) and the
+    build flags, to tell whether counter readings taken earlier still describe
+    the kernels being timed."""
     from moe_routed_expert_amd import build as hip_build
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[op]:
-        with open(os.path.join(hip_build.CSRC, name), "rb") as fh:
-            h.update(fh.read())
-    with open(os.path.join(ROOT, "include", "moe_epi.h"), "rb") as fh:
-        h.update(fh.read())
+        with open(os.path.join(hip_build.CSRC, name)) as fh:
+            h.update(_code_only(fh.read()).encode())
+    with open(os.path.join(ROOT, "include", "moe_epi.h")) as fh:
+        h.update(_code_only(fh.read()).encode())
     h.update(" ".join(hip_build.FLAGS).encode())
     return h.hexdigest()[:16]
 
