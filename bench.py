@@ -90,8 +90,8 @@ def parse_args():
 KERNEL_SOURCES = {
     "swiglu": ("swiglu_clamped.hip", "swiglu_math.h", "epi_common.h"),
     "router": ("router_weight_mul.hip", "epi_common.h"),
-    "grouped": ("grouped_swiglu.hip", "swiglu_math.h", "epi_common.h"),
-    "down": ("grouped_swiglu.hip", "swiglu_math.h", "epi_common.h"),
+    "grouped": ("grouped_swiglu.hip", "grouped_map.h", "swiglu_math.h", "epi_common.h"),
+    "down": ("grouped_swiglu.hip", "grouped_map.h", "swiglu_math.h", "epi_common.h"),
     "combine": ("moe_combine.hip", "epi_common.h"),
 }
 

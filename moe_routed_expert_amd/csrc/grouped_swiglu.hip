@@ -58,9 +58,11 @@
 // 128 x 128 blocks per CU (870-890), other read placements (1007-1049), a
 // branch-free unrolled loop (1022-1032), an L2 prefetch two to four steps
 // ahead (930), A tiles three stages deep (929), four wavefronts of 128-row
-// tiles (950), raised wave priority around the MFMAs (997). Timing with the in-loop loads removed gave 1430: waiting on
-// the loads of the next stage is the largest remaining cost.
+// tiles (950), raised wave priority around the MFMAs (997). Timing with the
+// in-loop loads removed gave 1430: waiting on the loads of the next stage is
+// the largest remaining cost.
 #include "epi_common.h"
+#include "grouped_map.h"
 #include "swiglu_math.h"
 
 namespace moe_epi {
@@ -68,50 +70,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-constexpr int kXcds = 8;  // MI355X: 8 XCDs, work-groups dispatched round-robin over them
-
-struct TileRows {
-    int64_t row0;   // first token of the tile
-    int rows;       // valid tokens in the tile (0: no tile)
-    int64_t expert;
-};
-
-// The mt-th row tile over all experts in order, each expert split into tiles
-// of bm rows (the last one partial). Uniform across the block.
-__device__ TileRows find_row_tile(const int32_t* __restrict__ offs, int64_t tokens, int64_t experts, int64_t mt,
-                                  int bm) {
-    int64_t start = 0, before = 0;
-    for (int64_t e = 0; e < experts; ++e) {
-        int64_t end = offs[e];
-        end = end < start ? start : (end > tokens ? tokens : end);
-        const int64_t n = (end - start + bm - 1) / bm;
-        if (mt < before + n) {
-            const int64_t row0 = start + (mt - before) * bm;
-            const int64_t left = end - row0;
-            return TileRows{row0, static_cast<int>(left < bm ? left : bm), e};
-        }
-        before += n;
-        start = end;
-    }
-    return TileRows{0, 0, 0};
-}
-
-// Logical tile -> (row tile, column tile). Tiles are visited in groups of gm
-// row tiles: within a group the row tile changes fastest, so the blocks that
-// run together on one XCD (consecutive logical tiles) cover about gm row
-// tiles x (concurrent / gm) column tiles, and reuse both their A tiles and
-// their weight tiles from L2 instead of streaming one and re-reading the other.
-__device__ __forceinline__ void tile_of(int64_t logical, int64_t m_tiles, int64_t n_tiles, int gm, int64_t* mt,
-                                        int64_t* nt) {
-    const int64_t per_group = static_cast<int64_t>(gm) * n_tiles;
-    const int64_t group = logical / per_group;
-    const int64_t first = group * gm;
-    const int64_t rows_in_group = m_tiles - first < gm ? m_tiles - first : gm;
-    const int64_t in_group = logical % per_group;
-    *mt = first + in_group % rows_in_group;
-    *nt = in_group / rows_in_group;
-}
 
 __device__ __forceinline__ float round_bf16(float v) { return __uint_as_float(static_cast<uint32_t>(to_bf16(v)) << 16); }
 
@@ -142,19 +100,6 @@ __device__ __forceinline__ void store_tile(const uint16_t* stage, uint16_t* __re
             *reinterpret_cast<u32x4*>(out + (row0 + row) * ld + col) =
                 *reinterpret_cast<const u32x4*>(stage + row * C::kLdo + cq * 8);
     }
-}
-
-// Grid: row tiles (worst case ceil(tokens / BM) + experts) times column
-// tiles, rounded up to a multiple of the XCD count. Returns 0 when it does not
-// fit a 1-D grid.
-template <class C>
-int64_t grouped_grid(int64_t tokens, int64_t n_cols, int64_t cols_per_tile, int64_t experts, int64_t* n_tiles,
-                     int64_t* n_blocks) {
-    *n_tiles = (n_cols + cols_per_tile - 1) / cols_per_tile;
-    const int64_t m_bound = (tokens + C::BM - 1) / C::BM + experts;
-    *n_blocks = m_bound * *n_tiles;
-    const int64_t grid = (*n_blocks + kXcds - 1) / kXcds * kXcds;
-    return grid < (static_cast<int64_t>(1) << 31) ? grid : 0;
 }
 
 // ---- the kernel -------------------------------------------------------------------
@@ -414,8 +359,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     constexpr int MI = C::MI, NI = C::NI, S = C::S;
     constexpr bool kRouter = kEpi != Epi::kSwiglu;
 
-    const int64_t per = static_cast<int64_t>(gridDim.x) / kXcds;
-    const int64_t logical = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+    const int64_t logical = xcd_contiguous(blockIdx.x, gridDim.x);
     if (logical >= n_blocks) return;
     int64_t mt, nt;
     tile_of(logical, n_blocks / n_tiles, n_tiles, C::GM, &mt, &nt);
@@ -540,7 +484,7 @@ int launch_grouped(const uint16_t* a, const uint16_t* w1, const uint16_t* w2, co
                    const float* probs, void* out, uint16_t* x_out, int64_t tokens, int64_t k_dim, int64_t n_dim,
                    int64_t experts, float limit, hipStream_t st) {
     int64_t n_tiles, n_blocks;
-    const int64_t grid = grouped_grid<C>(tokens, n_dim, kEpi == Epi::kSwiglu ? C::BN : 2 * C::BN, experts, &n_tiles,
+    const int64_t grid = grouped_grid(tokens, n_dim, kEpi == Epi::kSwiglu ? C::BN : 2 * C::BN, experts, C::BM, &n_tiles,
                                          &n_blocks);
     if (grid == 0) return MOE_EPI_ERR_BAD_SHAPE;
     (void)hipGetLastError();
