@@ -1,7 +1,9 @@
-// gate_up grouped GEMM with the clamped SwiGLU x probability epilogue, for
-// gfx950 (bf16 MFMA, fp32 accumulation).
+// Grouped GEMMs of the routed experts for gfx950 (bf16 MFMA, fp32
+// accumulation), one kernel template with two epilogues: the gate_up GEMM with
+// the clamped SwiGLU x probability epilogue, and the down projection with the
+// router-weight multiply epilogue (bf16 or fp32 output).
 //
-// Operation. Pages: "nemo_automodel.components.moe.mok_experts" (the routed
+// Operation (gate_up). Pages: "nemo_automodel.components.moe.mok_experts" (the routed
 // gate and up weights are contiguous bf16 [local_experts,
 // expert_intermediate, hidden]); "nemo_automodel.components.moe.
 // quantized_experts", MXFP4ExpertStorageMixin._mxfp4_base_mm (the routed
@@ -19,6 +21,17 @@
 // streaming forward computes it from a stored x. x = [gate | up] is written
 // too when the caller passes x_out (the backward's input). Rows at or past
 // the last end belong to no expert and are not written.
+//
+// Operation (down). Pages: "nemo_automodel.components.moe.mok_experts" (the
+// routed down weights are contiguous bf16 [local_experts, hidden,
+// expert_intermediate]); the grouped product as above;
+// "nemo_automodel.components.moe.optimized_ops", _apply_router_weight_fp32
+// (the product times the permuted probability in fp32, cast to the output
+// dtype). For a row t of local expert e:
+//   out2[t, n] = bf16(sum_i h[t, i] * w_down[e, n, i])   (fp32 accumulation)
+//   out[t, n]  = out_dtype(float(out2[t, n]) * p[t])
+// The block's two weight tiles are then two consecutive 128-column ranges of
+// w_down[e], so a block covers 256 output columns.
 //
 // Kernel shape (the launched configuration, Prod below):
 //   * A block computes a 256-token x 128-column tile of gate and the same
@@ -356,7 +369,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     uint16_t* __restrict__ x_out, int64_t tokens, int64_t k_dim, int64_t n_dim, int64_t experts, float L,
     int64_t n_tiles, int64_t n_blocks) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[C::kLdsElems];
-    constexpr int MI = C::MI, NI = C::NI, S = C::S;
+    constexpr int MI = C::MI, NI = C::NI;
     constexpr bool kRouter = kEpi != Epi::kSwiglu;
 
     const int64_t logical = xcd_contiguous(blockIdx.x, gridDim.x);
@@ -374,7 +387,8 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
 
     const uint16_t* a_tile = a + tr.row0 * k_dim;
     const uint16_t* g_tile = w1 + (tr.expert * n_dim + col1) * k_dim;
-    const uint16_t* u_tile = w2 + (tr.expert * n_dim + (ncols2 > 0 ? col2 : col1)) * k_dim;  // unread if ncols2 == 0
+    // with no second tile (ncols2 == 0) its loads repeat the first tile's rows and go unused
+    const uint16_t* u_tile = w2 + (tr.expert * n_dim + (ncols2 > 0 ? col2 : col1)) * k_dim;
 
     const int lane = static_cast<int>(threadIdx.x) % 64;
     const int wave = static_cast<int>(threadIdx.x) / 64;
