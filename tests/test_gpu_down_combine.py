@@ -267,3 +267,40 @@ def test_combine_full_size_sampled_tokens():
     want = oracle.moe_combine(d["expert_out"], code, row_of[idx], rows, idx.size, w.top_k, w.hidden)
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"{w.name}: sampled tokens differ"
     say(f"{w.name}: {idx.size} sampled tokens bit-exact")
+
+
+def test_the_chain_on_a_side_stream_gives_identical_results():
+    """gate_up GEMM + SwiGLU -> down GEMM + router multiply (fp32) -> combine, on the default
+    stream and on a side stream: bit-identical outputs (the binding passes the current stream)."""
+    from moe_routed_expert_amd.workloads import GroupedWorkload
+    gw = GroupedWorkload("chain", 1000, 256, 128, 4, 7.0, seed=41)
+    g = gw.generate()
+    rng = np.random.default_rng(42)
+    wd = to_dev_bf16(((rng.standard_normal((4, 256, 128)).astype(np.float32) * 0.05).view(np.uint32) >> 16)
+                     .astype(np.uint16))
+    a, wg, wu = to_dev_bf16(g["a"]), to_dev_bf16(g["w_gate"]), to_dev_bf16(g["w_up"])
+    offs = torch.from_numpy(g["offs"]).cuda()
+    p = torch.from_numpy(g["probs"]).cuda()
+    tokens, top_k = 500, 2
+    row_of = torch.from_numpy(rng.permutation(1000).astype(np.int32).reshape(tokens, top_k)).cuda()
+
+    def chain():
+        y = torch.empty((1000, 128), dtype=torch.bfloat16, device="cuda")
+        epi.grouped_gate_up_swiglu_fwd(a, wg, wu, offs, p, y, None, 7.0)
+        o = torch.empty((1000, 256), dtype=torch.float32, device="cuda")
+        epi.grouped_down_router_fwd(y, wd, offs, p, o)
+        c = torch.empty((tokens, 256), dtype=torch.float32, device="cuda")
+        epi.moe_combine_fwd(o, row_of, c)
+        return y, o, c
+
+    say("chain: default stream vs side stream")
+    ref = chain()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        got = chain()
+    torch.cuda.synchronize()
+    for r, q in zip(ref, got):
+        assert torch.equal(r.view(torch.int16) if r.dtype == torch.bfloat16 else r.view(torch.int32),
+                           q.view(torch.int16) if q.dtype == torch.bfloat16 else q.view(torch.int32))
+    assert torch.isfinite(ref[2]).all()
