@@ -277,6 +277,9 @@ void dispatch_fwd(const void* x, const float* probs, void* y, int64_t rows, int6
         return launch_fwd<T, 384, 1, 384>(x, probs, y, rows, inter, L, st);
     } else {
         if (nvec == 192) return launch_fwd<T, 256, 1, 512>(x, probs, y, rows, inter, L, st);
+        // a full 256-vector row (inter 2048): four rows per 1024-lane block ran at
+        // 81.7% of HBM peak against 80.5% with one row per block (bf16 and fp16 alike)
+        if (nvec == 256) return launch_fwd<T, 256, 1, 1024>(x, probs, y, rows, inter, L, st);
         if (nvec <= 256) return launch_fwd<T, 256, 1, 256>(x, probs, y, rows, inter, L, st);
         return launch_fwd<T, 1024, 1, 1024>(x, probs, y, rows, inter, L, st);
     }
