@@ -304,3 +304,91 @@ def test_the_chain_on_a_side_stream_gives_identical_results():
         assert torch.equal(r.view(torch.int16) if r.dtype == torch.bfloat16 else r.view(torch.int32),
                            q.view(torch.int16) if q.dtype == torch.bfloat16 else q.view(torch.int32))
     assert torch.isfinite(ref[2]).all()
+
+
+# ---- tensors of more than 2^31 elements (64-bit offsets) -----------------------------
+
+def _sampled_rows(tokens, offs, extra, seed):
+    rng = np.random.default_rng(seed)
+    ends = offs.astype(np.int64)
+    starts = np.concatenate([[0], ends[:-1]])
+    pick = {tokens - 1}
+    for s0, e0 in zip(starts, ends):
+        if e0 > s0:
+            pick |= {int(s0), int(e0 - 1)}
+    pick |= set(rng.integers(0, tokens, extra).tolist())
+    return np.array(sorted(pick))
+
+
+def test_gate_up_with_more_than_2_31_activation_elements():
+    tokens, hidden, inter, experts = 300000, 7168, 256, 2
+    offs = np.array([150001, tokens], np.int32)
+    g = torch.Generator(device="cuda").manual_seed(50)
+    say(f"gate_up {tokens}x{hidden}x{inter}: generate on the device")
+    a = torch.randn(tokens, hidden, device="cuda", generator=g).to(torch.bfloat16)
+    assert a.numel() > 2 ** 31
+    wg = (torch.randn(experts, inter, hidden, device="cuda", generator=g) * 0.05).to(torch.bfloat16)
+    wu = (torch.randn(experts, inter, hidden, device="cuda", generator=g) * 0.05).to(torch.bfloat16)
+    p = torch.rand(tokens, device="cuda", generator=g)
+    y = torch.empty(tokens, inter, dtype=torch.bfloat16, device="cuda")
+    x = torch.empty(tokens, 2 * inter, dtype=torch.bfloat16, device="cuda")
+    epi.grouped_gate_up_swiglu_fwd(a, wg, wu, torch.from_numpy(offs).cuda(), p, y, x, 10.0)
+    idx = _sampled_rows(tokens, offs, 60, 51)
+    ti = torch.from_numpy(idx).cuda()
+    a_s, x_s, y_s = to_host_bits(a[ti]), to_host_bits(x[ti]), to_host_bits(y[ti])
+    p_s = p[ti].cpu().numpy()
+    torch.cuda.synchronize()
+    expert_of = np.searchsorted(offs.astype(np.int64), idx, side="right")
+    sub_offs = np.array([np.sum(expert_of <= e) for e in range(experts)], dtype=np.int32)
+    say(f"gate_up: oracle on {idx.size} sampled rows (largest row offset {idx[-1] * hidden})")
+    s, s_abs = oracle.grouped_gate_up(a_s, to_host_bits(wg), to_host_bits(wu), sub_offs, idx.size, hidden, inter,
+                                      experts, with_abs_sum=True)
+    from tests.gpu_util import assert_bf16_parity, assert_gemm_bf16_within
+    assert_gemm_bf16_within(x_s, s, s_abs, hidden, "gate_up x beyond 2^31")
+    assert_bf16_parity(y_s, oracle.swiglu_clamped_fwd(x_s, p_s, idx.size, inter, 10.0), "gate_up y beyond 2^31")
+
+
+def test_down_with_more_than_2_31_output_elements():
+    tokens, inter, hidden, experts = 300000, 256, 7168, 2
+    offs = np.array([120000, tokens], np.int32)
+    g = torch.Generator(device="cuda").manual_seed(52)
+    say(f"down {tokens}x{inter}x{hidden}: generate on the device")
+    h = torch.randn(tokens, inter, device="cuda", generator=g).to(torch.bfloat16)
+    wd = (torch.randn(experts, hidden, inter, device="cuda", generator=g) * 0.1).to(torch.bfloat16)
+    p = torch.rand(tokens, device="cuda", generator=g)
+    out = torch.empty(tokens, hidden, dtype=torch.float32, device="cuda")
+    assert out.numel() > 2 ** 31
+    epi.grouped_down_router_fwd(h, wd, torch.from_numpy(offs).cuda(), p, out)
+    idx = _sampled_rows(tokens, offs, 60, 53)
+    ti = torch.from_numpy(idx).cuda()
+    h_s, o_s, p_s = to_host_bits(h[ti]), out[ti].cpu().numpy(), p[ti].cpu().numpy()
+    torch.cuda.synchronize()
+    expert_of = np.searchsorted(offs.astype(np.int64), idx, side="right")
+    sub_offs = np.array([np.sum(expert_of <= e) for e in range(experts)], dtype=np.int32)
+    say(f"down: oracle on {idx.size} sampled rows (largest output offset {idx[-1] * hidden})")
+    s, s_abs = exact_sums(h_s, to_host_bits(wd), sub_offs, idx.size, inter, hidden, experts)
+    assert_down_router_within(o_s, True, s, s_abs, p_s, inter, "down beyond 2^31")
+
+
+def test_combine_with_more_than_2_31_elements():
+    tokens, hidden, top_k = 300000, 7168, 2
+    rows = 320000
+    g = torch.Generator(device="cuda").manual_seed(54)
+    say(f"combine {tokens}x{hidden}, {rows} rows: generate on the device")
+    eo = torch.randn(rows, hidden, device="cuda", generator=g)
+    assert eo.numel() > 2 ** 31
+    rng = np.random.default_rng(55)
+    row_of = rng.integers(-1, rows, (tokens, top_k)).astype(np.int32)
+    row_of[-1] = [rows - 1, rows - 2]                     # the last rows, far past 2^31 elements
+    out = torch.empty(tokens, hidden, dtype=torch.float32, device="cuda")
+    epi.moe_combine_fwd(eo, torch.from_numpy(row_of).cuda(), out)
+    idx = np.unique(np.concatenate([rng.integers(0, tokens, 60), [tokens - 1]]))
+    used = np.unique(row_of[idx][row_of[idx] >= 0])
+    eo_s = eo[torch.from_numpy(used.astype(np.int64)).cuda()].cpu().numpy()
+    got = out[torch.from_numpy(idx).cuda()].cpu().numpy()
+    torch.cuda.synchronize()
+    remap = {int(r): i for i, r in enumerate(used)}
+    ro_s = np.vectorize(lambda r: remap.get(int(r), -1))(row_of[idx]).astype(np.int32)
+    say(f"combine: oracle on {idx.size} sampled tokens")
+    want = oracle.moe_combine(eo_s, oracle.F32, ro_s, used.size, idx.size, top_k, hidden)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), "combine beyond 2^31: sampled tokens differ"
