@@ -91,7 +91,8 @@ def test_swiglu_8192x2048(dt):
 @pytest.mark.parametrize("dt", ["f16", "f32"])
 @pytest.mark.parametrize("rows,inter,offset", [(37, 8, 0), (17, 136, 0), (9, 200, 0), (300, 1536, 0), (5, 2056, 0),
                                                (3, 8200, 0), (13, 24, 1), (7, 1544, 1), (2, 3, 0), (6, 1032, 0),
-                                               (9, 2048, 0), (4, 4096, 0), (3, 6144, 0), (2, 16384, 0), (5, 512, 0)])
+                                               (9, 2048, 0), (4, 4096, 0), (3, 6144, 0), (2, 16384, 0), (5, 512, 0),
+                                               (21, 1792, 0), (6, 2040, 0)])
 def test_swiglu_shapes(dt, rows, inter, offset):
     w = custom("swiglu", rows, inter, limit=7.0, x_sigma=5.0, seed=3000 + rows + inter,
                x_special_frac=0.1, x_special_values=(-7.0, 7.0, 0.0, 7.03125, -7.03125),

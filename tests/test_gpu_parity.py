@@ -149,11 +149,11 @@ def _offset_view(bits: np.ndarray, offset_elems: int) -> torch.Tensor:
 
 
 # Row widths reach every launch-shape bucket (vectors of 8 per row: < 64 with lane groups of 8, 16 and 32; 64;
-# 65-128; 129-191; 192; 193-256; 257-512; 513-1024; wider, in several passes), with ragged row counts, and the
+# 65-128; 129-191; 192; 193-255; 256; 257-512; 513-1024; wider, in several passes), with ragged row counts, and the
 # per-element path (widths not a multiple of 8; offset pointers).
 SHAPES = [(1, 1), (3, 3), (2, 8), (37, 8), (5, 24), (64, 56), (33, 64), (17, 136), (9, 200), (40, 520),
           (7, 1544), (5, 2056), (1031, 128), (300, 1536), (129, 2048), (11, 4096), (3, 8200), (6, 1032),
-          (4, 6144), (2, 16384), (5, 512), (3, 3072)]
+          (4, 6144), (2, 16384), (5, 512), (3, 3072), (21, 1792), (6, 2040)]
 
 
 @pytest.mark.parametrize("rows,inter", SHAPES)
