@@ -392,3 +392,26 @@ def test_combine_with_more_than_2_31_elements():
     say(f"combine: oracle on {idx.size} sampled tokens")
     want = oracle.moe_combine(eo_s, oracle.F32, ro_s, used.size, idx.size, top_k, hidden)
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), "combine beyond 2^31: sampled tokens differ"
+
+
+def test_router_multiply_to_fp32_then_combine_matches_the_oracle_bit_for_bit():
+    """The non-GEMM part of the path end to end: routed bf16 rows times their probabilities
+    into fp32 (router_weight_mul_fwd with an fp32 output), then the combine. Both steps are
+    exact definitions, so the chain must equal the oracle's chain bit for bit."""
+    w = COMBINE_WORKLOADS["combine_4096x1024_k8_e64of8"]
+    row_of, rows = w.row_of()
+    rng = np.random.default_rng(44)
+    xb = ((rng.standard_normal((rows, w.hidden)).astype(np.float32)).view(np.uint32) >> 16).astype(np.uint16)
+    p = rng.random(rows, dtype=np.float32)
+    say(f"router fp32 -> combine, {rows} rows x {w.hidden}")
+    x_d = to_dev_bf16(xb)
+    p_d = torch.from_numpy(p).cuda()
+    o_d = torch.empty((rows, w.hidden), dtype=torch.float32, device="cuda")
+    epi.router_weight_mul_fwd(x_d, p_d, o_d)
+    c_d = torch.empty((w.tokens, w.hidden), dtype=torch.float32, device="cuda")
+    epi.moe_combine_fwd(o_d, torch.from_numpy(row_of).cuda(), c_d)
+    torch.cuda.synchronize()
+    o_want = oracle.router_weight_mul_fwd_typed(xb, oracle.BF16, p, oracle.F32, rows, w.hidden)
+    c_want = oracle.moe_combine(o_want, oracle.F32, row_of, rows, w.tokens, w.top_k, w.hidden)
+    assert np.array_equal(o_d.cpu().numpy().view(np.uint32), o_want.view(np.uint32))
+    assert np.array_equal(c_d.cpu().numpy().view(np.uint32), c_want.view(np.uint32))
