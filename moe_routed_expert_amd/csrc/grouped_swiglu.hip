@@ -71,7 +71,9 @@
 // 128 x 128 blocks per CU (870-890), other read placements (1007-1049), a
 // branch-free unrolled loop (1022-1032), an L2 prefetch two to four steps
 // ahead (930), A tiles three stages deep (929), four wavefronts of 128-row
-// tiles (950), raised wave priority around the MFMAs (997). Timing with the
+// tiles (950), raised wave priority around the MFMAs (997), a ping-pong of
+// two wavefront groups alternating fragment-read and MFMA phases (885-925),
+// accumulators in AGPRs (no change). Timing with the
 // in-loop loads removed gave 1430: waiting on the loads of the next stage is
 // the largest remaining cost.
 #include "epi_common.h"
