@@ -25,6 +25,9 @@ Prints one JSON line. Options:
   --no-grad-probs    backward without the probability gradient (probabilities
                      that carry no gradient; the router then does not read x)
   --no-cpu-baseline  skip the oracle timing on the host
+  --all              the four SwiGLU workloads and the router workload in
+                     turn, one JSON line each (the default is the headline
+                     workload alone, one line)
   --workload grouped_* the gate_up grouped GEMM with the clamped SwiGLU
                      epilogue fused into it (one launch per step; x = [gate | up]
                      is written too, as the backward needs it, unless --no-x):
@@ -83,6 +86,8 @@ def parse_args():
     ap.add_argument("--cpu-threads", type=int, default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-x", action="store_true")
+    ap.add_argument("--all", action="store_true",
+                    help="every SwiGLU and router workload in turn, one JSON line each")
     return ap.parse_args()
 
 
@@ -197,9 +202,6 @@ def main():
               "with no exchange; per-GPU throughput is the figure. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
-    import torch
-
     import moe_routed_expert_amd as epi
     from moe_routed_expert_amd.workloads import HEADLINE, WORKLOADS
 
@@ -217,7 +219,21 @@ def main():
         return down_main(args, DOWN_WORKLOADS[args.workload])
     if args.workload in COMBINE_WORKLOADS:
         return combine_main(args, COMBINE_WORKLOADS[args.workload])
-    w = WORKLOADS[args.workload or HEADLINE]
+    if args.all:
+        for name in WORKLOADS:  # the five SwiGLU / router workloads, one line each
+            epilogue_main(args, WORKLOADS[name])
+        return None
+    return epilogue_main(args, WORKLOADS[args.workload or HEADLINE])
+
+
+def epilogue_main(args, w):
+    """One clamped-SwiGLU or router-weight-multiply workload: forward + backward per step."""
+    import numpy as np
+    import torch
+
+    import moe_routed_expert_amd as epi
+    from moe_routed_expert_amd.workloads import HEADLINE
+
     dt = args.dtype
     od = (args.out_dtype or dt) if w.op == "router" else dt
     want_gp = not args.no_grad_probs
