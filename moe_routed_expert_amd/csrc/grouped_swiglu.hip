@@ -73,9 +73,11 @@
 // ahead (930), A tiles three stages deep (929), four wavefronts of 128-row
 // tiles (950), raised wave priority around the MFMAs (997), a ping-pong of
 // two wavefront groups alternating fragment-read and MFMA phases (885-925),
-// accumulators in AGPRs (no change). Timing with the
-// in-loop loads removed gave 1430: waiting on the loads of the next stage is
-// the largest remaining cost.
+// accumulators in AGPRs (no change), the next step's loads spread between
+// the MFMAs of the current one (982-990). Timing-only copies: without the
+// in-loop loads 1430; with every load an L2 hit 1189; with the loads not
+// waited for, no change. The load instructions and the L2 misses cost about
+// equally; the waits at the barrier cost nothing measurable.
 #include "epi_common.h"
 #include "grouped_map.h"
 #include "swiglu_math.h"
