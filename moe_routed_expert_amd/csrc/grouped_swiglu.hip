@@ -74,7 +74,8 @@
 // tiles (950), raised wave priority around the MFMAs (997), a ping-pong of
 // two wavefront groups alternating fragment-read and MFMA phases (885-925),
 // accumulators in AGPRs (no change), the next step's loads spread between
-// the MFMAs of the current one (982-990). Timing-only copies: without the
+// the MFMAs of the current one (982-990), register-staged loads instead of
+// direct-to-LDS ones (775-823). Timing-only copies: without the
 // in-loop loads 1430; with every load an L2 hit 1189; with the loads not
 // waited for, no change. The load instructions and the L2 misses cost about
 // equally; the waits at the barrier cost nothing measurable.
