@@ -25,6 +25,9 @@ Prints one JSON line. Options:
   --no-grad-probs    backward without the probability gradient (probabilities
                      that carry no gradient; the router then does not read x)
   --no-cpu-baseline  skip the oracle timing on the host
+  --flush-cache      SwiGLU / router: a 1 GiB write before every launch, outside
+                     its events, evicts L2 and the 256 MB Infinity Cache; the
+                     step time is then the sum of the two kernels' event times
   --all              the four SwiGLU workloads and the router workload in
                      turn, one JSON line each (the default is the headline
                      workload alone, one line)
@@ -86,6 +89,8 @@ def parse_args():
     ap.add_argument("--cpu-threads", type=int, default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-x", action="store_true")
+    ap.add_argument("--flush-cache", action="store_true",
+                    help="SwiGLU / router: evict L2 and the Infinity Cache (1 GiB write) before every launch")
     ap.add_argument("--all", action="store_true",
                     help="every SwiGLU and router workload in turn, one JSON line each")
     return ap.parse_args()
@@ -274,22 +279,33 @@ def epilogue_main(args, w):
     torch.cuda.synchronize()
 
     E = lambda: torch.cuda.Event(enable_timing=True)
-    evs = [(E(), E(), E()) for _ in range(args.steps)]
+    evs = [(E(), E(), E(), E()) for _ in range(args.steps)]
+    # --flush-cache: a 1 GiB write before each launch evicts L2 and the 256 MB
+    # Infinity Cache, so that a workload smaller than them is not served from
+    # them; the flushes lie outside the kernels' events
+    scratch = torch.empty((1 << 28,), dtype=torch.float32, device=dev) if args.flush_cache else None
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1, e2 in evs:
+    for e0, e1, e2, e3 in evs:
+        if scratch is not None:
+            scratch.zero_()
         e0.record()
         fwd()
         e1.record()
-        bwd()
+        if scratch is not None:
+            scratch.zero_()
         e2.record()
+        bwd()
+        e3.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = np.array([a.elapsed_time(b) for a, b, _ in evs])
-    bwd_ms = np.array([b.elapsed_time(c) for _, b, c in evs])
+    fwd_ms = np.array([a.elapsed_time(b) for a, b, _, _ in evs])
+    bwd_ms = np.array([c.elapsed_time(d) for _, _, c, d in evs])
 
-    ms_per_step = wall * 1e3 / args.steps
+    # with flushes in the loop the step time is the two kernels' event time,
+    # otherwise the wall time of the whole timed region
+    ms_per_step = float((fwd_ms + bwd_ms).mean()) if scratch is not None else wall * 1e3 / args.steps
     value = (fwd_b + bwd_b) / (ms_per_step * 1e-3) / 1e9
 
     def kstats(name, nbytes, ms):
@@ -359,7 +375,8 @@ def epilogue_main(args, w):
         "config": {"workload": w.name, "op": w.op, "rows": rows,
                    ("inter" if w.op == "swiglu" else "hidden"): cols,
                    "limit": w.limit, "storage": dt, "output": od, "grad_probs": want_gp,
-                   "io": f"{dt} tensors, fp32 probs; fp32 arithmetic", "bytes_per_step": fwd_b + bwd_b},
+                   "io": f"{dt} tensors, fp32 probs; fp32 arithmetic", "bytes_per_step": fwd_b + bwd_b,
+                   "caches": "flushed before every launch" if args.flush_cache else "warm from the previous launch"},
         "frac_of_peak": value / PEAK_HBM_GBS,
         "kernels": kernels,
         "roofline": roofline,
