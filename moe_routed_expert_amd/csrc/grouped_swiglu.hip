@@ -33,7 +33,7 @@
 // The block's two weight tiles are then two consecutive 128-column ranges of
 // w_down[e], so a block covers 256 output columns.
 //
-// Kernel shape (the launched configuration, Prod below):
+// Kernel shape (the launched configurations, ProdGateUp and ProdDown below):
 //   * A block computes a 256-token x 128-column tile of gate and the same
 //     tile of up (so each output's gate and up sit in the same lane), with
 //     eight wavefronts (4 x 2) of 64 x 64 each: 2 x 2 v_mfma_f32_32x32x16_bf16
@@ -53,11 +53,13 @@
 //   * Tiles never straddle experts: each block finds its expert and row range
 //     from offs on the device (no host copy of offs), so a grid sized for
 //     the worst case, ceil(tokens / 256) + experts row tiles, covers any split.
-//   * XCD-aware order: consecutive block ids land on different XCDs, so the
-//     block id is remapped to give each XCD a contiguous range of tiles, and
-//     those are visited in groups of 4 row tiles, so that the blocks running
-//     together on one XCD share both their A tiles and their weight tiles in
-//     that XCD's L2.
+//   * Tile order: tiles are visited in groups of 4 row tiles, so that the
+//     blocks running together on one XCD share both their A tiles and their
+//     weight tiles in that XCD's L2. Consecutive block ids land on different
+//     XCDs; the down projection remaps the block id to give each XCD a
+//     contiguous range of tiles, the gate_up GEMM keeps the hardware's
+//     round-robin placement, so that all 8 XCDs work on neighbouring tiles of
+//     the same expert and its re-reads hit the shared Infinity Cache.
 //   * Epilogue: accumulators are rounded to bf16, the SwiGLU is applied, and
 //     each output tile is staged through LDS so that global stores are
 //     16-byte, row-contiguous accesses.
@@ -66,7 +68,8 @@
 // register-staged loads with padded LDS ran at 746-918 TFLOP/s over 22 tile
 // shapes, deeper load pipelines and fragment pipelining at up to 953, the
 // same tiles with one barrier per step at 941-965, and this loop at 1040-1060
-// (MFMA busy 54% of cycles, LDS 21%, bank conflicts 0.8% of LDS cycles).
+// (MFMA busy 54% of cycles, LDS 21%, bank conflicts 0.8% of LDS cycles) with
+// the XCD-contiguous block order, 1090-1108 with the round-robin one.
 // Variants that did not help: K steps of 32 with 3-5 stages (850-912), two
 // 128 x 128 blocks per CU (870-890), other read placements (1007-1049), a
 // branch-free unrolled loop (1022-1032), an L2 prefetch two to four steps
@@ -128,9 +131,10 @@ __device__ __forceinline__ void store_tile(const uint16_t* stage, uint16_t* __re
 // of LDS contiguously, so tiles are not padded: chunk kq of a row (BK / 8
 // chunks of 16 bytes) is placed at slot row * (BK / 8) + (kq ^ swz(row)),
 // which keeps the 16-byte fragment reads conflict-free.
-template <int BM_, int BN_, int WM_, int WN_, int S_, int OCC_, int GM_ = 1, int BK_ = 32>
+template <int BM_, int BN_, int WM_, int WN_, int S_, int OCC_, int GM_ = 1, int BK_ = 32, bool XCD_ = true>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, S = S_, OCC = OCC_, GM = GM_;
+    static constexpr bool kXcdOrder = XCD_;  // give each XCD a contiguous range of tiles
     static constexpr int kCpr = BK / 8;                // 16-byte chunks per row
     static_assert(kCpr == 4 || kCpr == 8, "K steps of 32 or 64");
     static constexpr int kThreads = 64 * WM * WN;
@@ -150,8 +154,16 @@ struct Cfg {
     static_assert(BM * BN % (8 * kThreads) == 0, "whole output chunks per thread");
 };
 
-// The configuration the library launches (see the kernel-shape notes at the top).
-using Prod = Cfg<256, 128, 4, 2, 2, 2, 4, 64>;
+// The configurations the library launches (see the kernel-shape notes at the
+// top). They differ only in the block order: the down projection gives each
+// XCD a contiguous range of tiles, the gate_up GEMM keeps the hardware's
+// round-robin placement, so that all XCDs work on the same expert's tiles at
+// once and share its weight and activation re-reads in the Infinity Cache
+// (gate_up at 131072 x 7168 x 2048: 1107 TFLOP/s against 1061 with the
+// XCD-contiguous order; the down projection at 131072 x 2048 x 7168: 1027
+// against 1007 the other way round).
+using ProdGateUp = Cfg<256, 128, 4, 2, 2, 2, 4, 64, false>;
+using ProdDown = Cfg<256, 128, 4, 2, 2, 2, 4, 64, true>;
 
 // Swizzle of a row's chunks: any 8 consecutive rows, and any 16 consecutive
 // rows taken 4 or 8 apart, put the same chunk in different 16-byte bank groups.
@@ -377,7 +389,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     constexpr int MI = C::MI, NI = C::NI;
     constexpr bool kRouter = kEpi != Epi::kSwiglu;
 
-    const int64_t logical = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int64_t logical = C::kXcdOrder ? xcd_contiguous(blockIdx.x, gridDim.x) : static_cast<int64_t>(blockIdx.x);
     if (logical >= n_blocks) return;
     int64_t mt, nt;
     tile_of(logical, n_blocks / n_tiles, n_tiles, C::GM, &mt, &nt);
@@ -569,7 +581,7 @@ extern "C" int grouped_gate_up_swiglu_fwd(const uint16_t* a, const uint16_t* w_g
         if (overlaps(out, ra) || overlaps(out, rg) || overlaps(out, ru) || overlaps(out, ro) || overlaps(out, rp))
             return MOE_EPI_ERR_ALIAS;
     if (overlaps(ry, rx)) return MOE_EPI_ERR_ALIAS;
-    return launch_grouped<Prod, Epi::kSwiglu>(a, w_gate, w_up, offs, probs, y, x_out, tokens, hidden, inter, experts,
+    return launch_grouped<ProdGateUp, Epi::kSwiglu>(a, w_gate, w_up, offs, probs, y, x_out, tokens, hidden, inter, experts,
                                               limit, as_stream(stream));
 }
 
@@ -596,8 +608,8 @@ extern "C" int grouped_down_router_fwd(const uint16_t* h, const uint16_t* w_down
         overlaps(ro, range_of(probs, pb)))
         return MOE_EPI_ERR_ALIAS;
     if (out_dtype == MOE_EPI_F32)
-        return launch_grouped<Prod, Epi::kRouterF32>(h, w_down, w_down, offs, probs, out, nullptr, tokens, inter,
+        return launch_grouped<ProdDown, Epi::kRouterF32>(h, w_down, w_down, offs, probs, out, nullptr, tokens, inter,
                                                      hidden, experts, 1.0f, as_stream(stream));
-    return launch_grouped<Prod, Epi::kRouterBf16>(h, w_down, w_down, offs, probs, out, nullptr, tokens, inter, hidden,
+    return launch_grouped<ProdDown, Epi::kRouterBf16>(h, w_down, w_down, offs, probs, out, nullptr, tokens, inter, hidden,
                                                   experts, 1.0f, as_stream(stream));
 }

@@ -1,8 +1,9 @@
 """The grouped GEMM's block -> tile mapping (csrc/grouped_map.h), checked on the CPU.
 
 A host-only build of the library's own header walks every block of the launched grid
-the way the kernel does: the XCD remap of the block id, the grouped tile order
-(tile_of) and the search for the row tile's expert and rows (find_row_tile).
+the way the kernel does: the block order (the hardware's, or the XCD remap of the
+block id), the grouped tile order (tile_of) and the search for the row tile's expert
+and rows (find_row_tile).
 For random and malformed token counts per expert, both epilogue widths and
 several group sizes, every row of every expert must be covered exactly once
 per column tile, rows of no expert never, no tile may straddle two experts or
@@ -25,7 +26,7 @@ using namespace moe_epi;
 
 // 0 on success, else a code naming the first violation
 // the launched tile: 256 rows x 128 columns per weight tensor (x 2 in router mode)
-template <int GM>
+template <int GM, bool XCD>
 int walk(const std::vector<int32_t>& offs, int64_t tokens, int64_t n_cols, bool router) {
     constexpr int BM = 256, BN = 128;
     const int64_t experts = static_cast<int64_t>(offs.size());
@@ -44,7 +45,7 @@ int walk(const std::vector<int32_t>& offs, int64_t tokens, int64_t n_cols, bool 
     std::vector<int> seen(static_cast<size_t>(tokens * n_tiles), 0);
     std::vector<char> hit(grid, 0);
     for (int64_t b = 0; b < grid; ++b) {
-        const int64_t logical = xcd_contiguous(b, grid);
+        const int64_t logical = XCD ? xcd_contiguous(b, grid) : b;
         if (logical < 0 || logical >= grid || hit[logical]) return 2;
         hit[logical] = 1;
         if (logical >= n_blocks) continue;
@@ -102,9 +103,11 @@ def test_every_row_covered_once_per_column_tile(tmp_path):
         vec = "{" + ", ".join(str(v) for v in offs) + "}"
         for n_cols, router in ((128, False), (136, False), (2048, False), (256, True), (264, True), (120, True)):
             for gm in (1, 4, 8):
-                calls.append(f"    {{ int r = walk<{gm}>(std::vector<int32_t>{vec}, {tokens}, {n_cols}, {str(router).lower()}); "
-                             f"++n; if (r) {{ ++bad; printf(\"tokens=%d cols=%d router=%d gm=%d: code %d\\n\", {tokens}, "
-                             f"{n_cols}, {int(router)}, {gm}, r); }} }}")
+                for xcd in ("true", "false"):
+                    calls.append(f"    {{ int r = walk<{gm}, {xcd}>(std::vector<int32_t>{vec}, {tokens}, {n_cols}, "
+                                 f"{str(router).lower()}); ++n; if (r) {{ ++bad; printf(\"tokens=%d cols=%d router=%d "
+                                 f"gm=%d xcd=%d: code %d\\n\", {tokens}, {n_cols}, {int(router)}, {gm}, "
+                                 f"{int(xcd == 'true')}, r); }} }}")
     src = tmp_path / "tilemap.cpp"
     src.write_text(SOURCE.replace("@CALLS@", "\n".join(calls)))
     exe = tmp_path / "tilemap"
