@@ -14,8 +14,6 @@
 
 namespace moe_epi {
 
-constexpr int kXcds = 8;  // MI355X: 8 XCDs, work-groups dispatched round-robin over them
-
 struct TileRows {
     int64_t row0;   // first token of the tile
     int rows;       // valid tokens in the tile (0: no tile)
@@ -42,10 +40,13 @@ __host__ __device__ inline TileRows find_row_tile(const int32_t* __restrict__ of
 }
 
 // Logical tile -> (row tile, column tile). Tiles are visited in groups of gm
-// row tiles: within a group the row tile changes fastest, so the blocks that
-// run together on one XCD (consecutive logical tiles) cover about gm row
-// tiles x (concurrent / gm) column tiles, and reuse both their A tiles and
-// their weight tiles from L2 instead of streaming one and re-reading the other.
+// row tiles: within a group the row tile changes fastest. Blocks are handed
+// to the 8 XCDs in turn, so the blocks that run together on one XCD are every
+// 8th logical tile of a window of consecutive ones; that window covers a few
+// groups' row tiles and a run of column tiles, and each XCD's share of it
+// reuses both its A tiles and its weight tiles from L2 instead of streaming
+// one and re-reading the other. All XCDs work on the same window, so their
+// L2 misses meet in the shared Infinity Cache.
 __host__ __device__ inline void tile_of(int64_t logical, int64_t m_tiles, int64_t n_tiles, int gm, int64_t* mt,
                                         int64_t* nt) {
     const int64_t per_group = static_cast<int64_t>(gm) * n_tiles;
@@ -57,23 +58,15 @@ __host__ __device__ inline void tile_of(int64_t logical, int64_t m_tiles, int64_
     *nt = in_group / rows_in_group;
 }
 
-// Consecutive block ids land on different XCDs; this remap gives XCD x the
-// contiguous logical range [x * grid / kXcds, (x + 1) * grid / kXcds). A
-// bijection of [0, grid) when grid is a multiple of kXcds.
-__host__ __device__ inline int64_t xcd_contiguous(int64_t block, int64_t grid) {
-    return (block % kXcds) * (grid / kXcds) + block / kXcds;
-}
-
 // Grid: row tiles (worst case ceil(tokens / bm) + experts: one partial tile
-// per expert) times column tiles, rounded up to a multiple of the XCD count.
+// per expert) times column tiles.
 // Returns 0 when it does not fit a 1-D grid.
 inline int64_t grouped_grid(int64_t tokens, int64_t n_cols, int64_t cols_per_tile, int64_t experts, int bm,
                             int64_t* n_tiles, int64_t* n_blocks) {
     *n_tiles = (n_cols + cols_per_tile - 1) / cols_per_tile;
     const int64_t m_bound = (tokens + bm - 1) / bm + experts;
     *n_blocks = m_bound * *n_tiles;
-    const int64_t grid = (*n_blocks + kXcds - 1) / kXcds * kXcds;
-    return grid < (static_cast<int64_t>(1) << 31) ? grid : 0;
+    return *n_blocks < (static_cast<int64_t>(1) << 31) ? *n_blocks : 0;
 }
 
 }  // namespace moe_epi

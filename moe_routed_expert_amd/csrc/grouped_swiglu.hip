@@ -53,13 +53,16 @@
 //   * Tiles never straddle experts: each block finds its expert and row range
 //     from offs on the device (no host copy of offs), so a grid sized for
 //     the worst case, ceil(tokens / 256) + experts row tiles, covers any split.
-//   * Tile order: tiles are visited in groups of 4 row tiles, so that the
+//   * Tile order: tiles are visited in groups of row tiles (4 for gate_up, 32
+//     for the down projection), the row tile changing fastest, so that the
 //     blocks running together on one XCD share both their A tiles and their
-//     weight tiles in that XCD's L2. Consecutive block ids land on different
-//     XCDs; the down projection remaps the block id to give each XCD a
-//     contiguous range of tiles, the gate_up GEMM keeps the hardware's
-//     round-robin placement, so that all 8 XCDs work on neighbouring tiles of
-//     the same expert and its re-reads hit the shared Infinity Cache.
+//     weight tiles in that XCD's L2. The hardware hands consecutive block ids
+//     to the 8 XCDs in turn, and the kernel keeps that placement: all XCDs
+//     then work on neighbouring tiles of the same expert, and their L2 misses
+//     on its weights and activations hit the shared Infinity Cache. Giving
+//     each XCD a contiguous range of tiles instead puts the XCDs on different
+//     experts: gate_up 1061 TFLOP/s against 1107, the down projection 1008
+//     against 1023.
 //   * Epilogue: accumulators are rounded to bf16, the SwiGLU is applied, and
 //     each output tile is staged through LDS so that global stores are
 //     16-byte, row-contiguous accesses.
@@ -69,7 +72,7 @@
 // shapes, deeper load pipelines and fragment pipelining at up to 953, the
 // same tiles with one barrier per step at 941-965, and this loop at 1040-1060
 // (MFMA busy 54% of cycles, LDS 21%, bank conflicts 0.8% of LDS cycles) with
-// the XCD-contiguous block order, 1090-1108 with the round-robin one.
+// an XCD-contiguous block order, 1090-1108 with the round-robin one.
 // Variants that did not help: K steps of 32 with 3-5 stages (850-912), two
 // 128 x 128 blocks per CU (870-890), other read placements (1007-1049), a
 // branch-free unrolled loop (1022-1032), an L2 prefetch two to four steps
@@ -131,10 +134,9 @@ __device__ __forceinline__ void store_tile(const uint16_t* stage, uint16_t* __re
 // of LDS contiguously, so tiles are not padded: chunk kq of a row (BK / 8
 // chunks of 16 bytes) is placed at slot row * (BK / 8) + (kq ^ swz(row)),
 // which keeps the 16-byte fragment reads conflict-free.
-template <int BM_, int BN_, int WM_, int WN_, int S_, int OCC_, int GM_ = 1, int BK_ = 32, bool XCD_ = true>
+template <int BM_, int BN_, int WM_, int WN_, int S_, int OCC_, int GM_ = 1, int BK_ = 32>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, S = S_, OCC = OCC_, GM = GM_;
-    static constexpr bool kXcdOrder = XCD_;  // give each XCD a contiguous range of tiles
     static constexpr int kCpr = BK / 8;                // 16-byte chunks per row
     static_assert(kCpr == 4 || kCpr == 8, "K steps of 32 or 64");
     static constexpr int kThreads = 64 * WM * WN;
@@ -155,15 +157,12 @@ struct Cfg {
 };
 
 // The configurations the library launches (see the kernel-shape notes at the
-// top). They differ only in the block order: the down projection gives each
-// XCD a contiguous range of tiles, the gate_up GEMM keeps the hardware's
-// round-robin placement, so that all XCDs work on the same expert's tiles at
-// once and share its weight and activation re-reads in the Infinity Cache
-// (gate_up at 131072 x 7168 x 2048: 1107 TFLOP/s against 1061 with the
-// XCD-contiguous order; the down projection at 131072 x 2048 x 7168: 1027
-// against 1007 the other way round).
-using ProdGateUp = Cfg<256, 128, 4, 2, 2, 2, 4, 64, false>;
-using ProdDown = Cfg<256, 128, 4, 2, 2, 2, 4, 64, true>;
+// top). They differ only in the tile group: 4 row tiles for the gate_up GEMM
+// (16 column tiles at inter 2048), 32 for the down projection (28 column
+// tiles at hidden 7168), each the best of a sweep (gate_up: 2-4 row tiles
+// 1107 TFLOP/s, 1 1094, 16 1079; down: 32 1023, 4 1011, 14 999, 7 968).
+using ProdGateUp = Cfg<256, 128, 4, 2, 2, 2, 4, 64>;
+using ProdDown = Cfg<256, 128, 4, 2, 2, 2, 32, 64>;
 
 // Swizzle of a row's chunks: any 8 consecutive rows, and any 16 consecutive
 // rows taken 4 or 8 apart, put the same chunk in different 16-byte bank groups.
@@ -389,7 +388,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     constexpr int MI = C::MI, NI = C::NI;
     constexpr bool kRouter = kEpi != Epi::kSwiglu;
 
-    const int64_t logical = C::kXcdOrder ? xcd_contiguous(blockIdx.x, gridDim.x) : static_cast<int64_t>(blockIdx.x);
+    const int64_t logical = blockIdx.x;
     if (logical >= n_blocks) return;
     int64_t mt, nt;
     tile_of(logical, n_blocks / n_tiles, n_tiles, C::GM, &mt, &nt);

@@ -1,13 +1,13 @@
 """The grouped GEMM's block -> tile mapping (csrc/grouped_map.h), checked on the CPU.
 
 A host-only build of the library's own header walks every block of the launched grid
-the way the kernel does: the block order (the hardware's, or the XCD remap of the
-block id), the grouped tile order (tile_of) and the search for the row tile's expert
-and rows (find_row_tile).
+the way the kernel does: the grouped tile order (tile_of, for the group sizes the
+kernels use and others) and the search for the row tile's expert and rows
+(find_row_tile).
 For random and malformed token counts per expert, both epilogue widths and
 several group sizes, every row of every expert must be covered exactly once
 per column tile, rows of no expert never, no tile may straddle two experts or
-exceed the tile height, and the remap must be a bijection of the grid.
+exceed the tile height, and every block of the grid must be visited once.
 """
 import os
 import shutil
@@ -26,13 +26,13 @@ using namespace moe_epi;
 
 // 0 on success, else a code naming the first violation
 // the launched tile: 256 rows x 128 columns per weight tensor (x 2 in router mode)
-template <int GM, bool XCD>
+template <int GM>
 int walk(const std::vector<int32_t>& offs, int64_t tokens, int64_t n_cols, bool router) {
     constexpr int BM = 256, BN = 128;
     const int64_t experts = static_cast<int64_t>(offs.size());
     int64_t n_tiles, n_blocks;
     const int64_t grid = grouped_grid(tokens, n_cols, router ? 2 * BN : BN, experts, BM, &n_tiles, &n_blocks);
-    if (grid <= 0 || grid % kXcds != 0 || grid < n_blocks) return 1;
+    if (grid <= 0 || grid != n_blocks) return 1;
     // expert of each row (-1: none), as the pages define the ranges
     std::vector<int64_t> expert_of(tokens, -1);
     int64_t start = 0;
@@ -45,8 +45,8 @@ int walk(const std::vector<int32_t>& offs, int64_t tokens, int64_t n_cols, bool 
     std::vector<int> seen(static_cast<size_t>(tokens * n_tiles), 0);
     std::vector<char> hit(grid, 0);
     for (int64_t b = 0; b < grid; ++b) {
-        const int64_t logical = XCD ? xcd_contiguous(b, grid) : b;
-        if (logical < 0 || logical >= grid || hit[logical]) return 2;
+        const int64_t logical = b;  // the kernel keeps the hardware's block order
+        if (hit[logical]) return 2;
         hit[logical] = 1;
         if (logical >= n_blocks) continue;
         int64_t mt, nt;
@@ -102,12 +102,10 @@ def test_every_row_covered_once_per_column_tile(tmp_path):
     for tokens, offs in cases():
         vec = "{" + ", ".join(str(v) for v in offs) + "}"
         for n_cols, router in ((128, False), (136, False), (2048, False), (256, True), (264, True), (120, True)):
-            for gm in (1, 4, 8):
-                for xcd in ("true", "false"):
-                    calls.append(f"    {{ int r = walk<{gm}, {xcd}>(std::vector<int32_t>{vec}, {tokens}, {n_cols}, "
-                                 f"{str(router).lower()}); ++n; if (r) {{ ++bad; printf(\"tokens=%d cols=%d router=%d "
-                                 f"gm=%d xcd=%d: code %d\\n\", {tokens}, {n_cols}, {int(router)}, {gm}, "
-                                 f"{int(xcd == 'true')}, r); }} }}")
+            for gm in (1, 4, 8, 32):
+                calls.append(f"    {{ int r = walk<{gm}>(std::vector<int32_t>{vec}, {tokens}, {n_cols}, "
+                             f"{str(router).lower()}); ++n; if (r) {{ ++bad; printf(\"tokens=%d cols=%d router=%d "
+                             f"gm=%d: code %d\\n\", {tokens}, {n_cols}, {int(router)}, {gm}, r); }} }}")
     src = tmp_path / "tilemap.cpp"
     src.write_text(SOURCE.replace("@CALLS@", "\n".join(calls)))
     exe = tmp_path / "tilemap"
