@@ -103,6 +103,8 @@ def test_small_named_workloads(name):
     (300, 64, 256, 3, "dirichlet"), (257, 200, 136, 4, "one_empty"), (1000, 256, 512, 1, "even"),
     (129, 96, 120, 7, "dirichlet"), (640, 1032, 376, 16, "dirichlet"), (1, 8, 8, 1, "even"),
     (513, 2048, 264, 2, "dirichlet"),
+    # many experts: more row tiles than one tile group holds, groups spanning experts
+    (3000, 128, 1024, 64, "dirichlet"),
 ])
 def test_down_shapes(tokens, inter, hidden, experts, split):
     w = DownWorkload(f"d_{tokens}x{inter}x{hidden}_e{experts}", tokens, inter, hidden, experts,
@@ -117,6 +119,13 @@ def test_down_counts_that_are_empty_decreasing_or_too_large(offs):
     d = w.generate()
     d["offs"] = np.array(offs, dtype=np.int32)
     check_down(d, 257, 64, 40, 4, f"offs {offs}")
+
+
+def test_down_every_token_in_one_expert_of_sixteen():
+    w = DownWorkload("d_skew", 2000, 96, 520, 16, seed=35)
+    d = w.generate()
+    d["offs"] = np.array([0] * 7 + [2000] * 9, dtype=np.int32)
+    check_down(d, 2000, 96, 520, 16, "one expert holds every token")
 
 
 def test_down_zero_probabilities_and_zero_rows():

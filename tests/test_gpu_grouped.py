@@ -87,6 +87,8 @@ def test_small_named_workload():
 @pytest.mark.parametrize("tokens,hidden,inter,experts,split", [
     (300, 64, 128, 3, "dirichlet"), (257, 200, 136, 4, "one_empty"), (1000, 512, 256, 1, "even"),
     (129, 96, 8, 7, "dirichlet"), (640, 1032, 264, 16, "dirichlet"), (1, 8, 8, 1, "even"),
+    # many experts: dozens of partial row tiles, the grid's tile groups span experts
+    (3000, 128, 512, 64, "dirichlet"),
 ])
 def test_shapes(tokens, hidden, inter, experts, split):
     w = GroupedWorkload(f"g_{tokens}x{hidden}x{inter}_e{experts}", tokens, hidden, inter, experts, 7.0,
@@ -101,6 +103,15 @@ def test_counts_that_are_empty_decreasing_or_too_large(offs):
     d = w.generate()
     d["offs"] = np.array(offs, dtype=np.int32)
     check(d, 257, 64, 32, 4, 7.0, f"offs {offs}")
+
+
+def test_every_token_in_one_expert_of_sixteen():
+    # all other experts empty, before and after it: their row ranges are empty and
+    # the grid's worst-case row tiles beyond the real ones exit without writing
+    w = GroupedWorkload("g_skew", 2000, 96, 256, 16, 7.0, seed=34)
+    d = w.generate()
+    d["offs"] = np.array([0] * 7 + [2000] * 9, dtype=np.int32)
+    check(d, 2000, 96, 256, 16, 7.0, "one expert holds every token")
 
 
 def test_full_size_sampled_rows():
