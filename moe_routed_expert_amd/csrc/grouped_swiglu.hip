@@ -49,7 +49,8 @@
 //     barrier per K step, before the last sub-step, a bare s_barrier after
 //     explicit waits (a __syncthreads() fence would also wait for the loads
 //     still in flight); the loads of the step after next and the next step's
-//     first fragments are issued while the last sub-step's MFMAs run.
+//     first fragments are issued while the last sub-step's MFMAs run, one
+//     MFMA, one load, one read at a time, the loads in buffer form.
 //   * Tiles never straddle experts: each block finds its expert and row range
 //     from offs on the device (no host copy of offs), so a grid sized for
 //     the worst case, ceil(tokens / 256) + experts row tiles, covers any split.
@@ -72,7 +73,8 @@
 // shapes, deeper load pipelines and fragment pipelining at up to 953, the
 // same tiles with one barrier per step at 941-965, and this loop at 1040-1060
 // (MFMA busy 54% of cycles, LDS 21%, bank conflicts 0.8% of LDS cycles) with
-// an XCD-contiguous block order, 1090-1108 with the round-robin one.
+// an XCD-contiguous block order, 1090-1108 with the round-robin one, and
+// 1174-1202 with the last sub-step's loads interleaved between its MFMAs.
 // Variants that did not help: K steps of 32 with 3-5 stages (850-912), two
 // 128 x 128 blocks per CU (870-890), other read placements (1007-1049), a
 // branch-free unrolled loop (1022-1032), an L2 prefetch two to four steps
@@ -81,10 +83,10 @@
 // two wavefront groups alternating fragment-read and MFMA phases (885-925),
 // accumulators in AGPRs (no change), the next step's loads spread between
 // the MFMAs of the current one (982-990), register-staged loads instead of
-// direct-to-LDS ones (775-823). Timing-only copies with the round-robin
-// order: MFMAs, barriers and epilogue alone 1677, plus the fragment reads
-// 1475, plus loads that all hit L2 1198, as launched 1100; the loads not
-// waited for at the barrier: no change. The shader clock averages about
+// direct-to-LDS ones (775-823), A tiles three stages deep (962). Timing-only
+// copies before the interleave: MFMAs, barriers and epilogue alone 1677, plus
+// the fragment reads 1475, plus loads that all hit L2 1198, as launched 1100;
+// the loads not waited for at the barrier: no change. The shader clock averages about
 // 1.74 GHz in this kernel (busy cycles per XCD over the dispatch time), so
 // 2.5 PFLOP/s at 2.4 GHz is about 1.81 PFLOP/s at the clock it runs at.
 #include "epi_common.h"
@@ -248,6 +250,49 @@ struct PipeLoads {
     __device__ __forceinline__ static void load(const uint16_t* src, uint16_t* dst) {
         __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
+
+    // The same loads in buffer form (buffer_load_dwordx4 ... lds): the tile's
+    // base in a scalar resource and each chunk's byte offset in one 32-bit
+    // register, so a full K step needs no 64-bit address arithmetic and fewer
+    // registers. Valid while every offset stays below 2^31 (kBufMaxK).
+    struct Buf {
+        __amdgpu_buffer_rsrc_t ra, rg, ru;
+        uint32_t va[kA], vg[kW], vu[kW];
+    };
+    __device__ __forceinline__ Buf buffers(const uint16_t* a_tile, const uint16_t* g_tile,
+                                           const uint16_t* u_tile) const {
+        // dword 3 of the resource: 32-bit data format, no swizzle, as gfx9 buffer loads expect
+        constexpr int kFlags = 0x00020000;
+        Buf b;
+        b.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a_tile), 0, 0x7FFFFFFF, kFlags);
+        b.rg = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(g_tile), 0, 0x7FFFFFFF, kFlags);
+        b.ru = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(u_tile), 0, 0x7FFFFFFF, kFlags);
+#pragma unroll
+        for (int i = 0; i < kA; ++i) b.va[i] = static_cast<uint32_t>((pa[i] - a_tile) * 2);
+#pragma unroll
+        for (int i = 0; i < kW; ++i) {
+            b.vg[i] = static_cast<uint32_t>((pg[i] - g_tile) * 2);
+            b.vu[i] = static_cast<uint32_t>((pu[i] - u_tile) * 2);
+        }
+        return b;
+    }
+    // Load number i (A chunks first, then gate/up pairs) of full K step kt into stage st.
+    __device__ __forceinline__ void issue_one(const Buf& b, uint16_t* st, int64_t kt, int i) const {
+        const int soff = static_cast<int>(kt * C::BK * 2);
+        auto bl = [&](__amdgpu_buffer_rsrc_t r, uint32_t voff, uint16_t* dst) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff,
+                                                     0, 0);
+        };
+        if (i < kA) {
+            bl(b.ra, b.va[i], st + oa[i] * 8);
+        } else {
+            const int j = (i - kA) / 2;
+            if ((i - kA) % 2 == 0)
+                bl(b.rg, b.vg[j], st + C::kAElems + ow[j] * 8);
+            else
+                bl(b.ru, b.vu[j], st + C::kAElems + C::kWElems + ow[j] * 8);
+        }
+    }
     __device__ __forceinline__ static void zero(uint16_t* dst) {
         *reinterpret_cast<u32x4*>(dst) = u32x4{0u, 0u, 0u, 0u};
     }
@@ -289,7 +334,7 @@ struct PipeLoads {
     }
 };
 
-template <class C>
+template <class C, bool kBuf>
 __device__ __forceinline__ void mainloop_pipe(uint16_t* lds, const uint16_t* a_tile, const uint16_t* g_tile,
                                               const uint16_t* u_tile, int arows, int grows, int urows,
                                               int64_t k_dim, f32x16 (&acc_g)[C::MI][C::NI],
@@ -347,7 +392,58 @@ __device__ __forceinline__ void mainloop_pipe(uint16_t* lds, const uint16_t* a_t
     if (nk > 1) ld.issue(lds + C::kStageElems, 1, k_dim);
     read(lds, 0, 0);
 
-    for (int64_t kt = 0; kt < nk; ++kt) {
+    int64_t kt = 0;
+    if constexpr (kBuf) {
+        // While the step after next is a full K step, the last sub-step issues
+        // its loads in buffer form one after each MFMA, with the next step's
+        // first fragment reads in between, in a branch-free loop body. Issued
+        // together before the MFMAs, the loads held the wavefronts at issue
+        // while the MFMA units idled (1072 against 1174 TFLOP/s for gate_up).
+        constexpr int kLoads = C::kAChunks + 2 * C::kWChunks, kReads = MI + 2 * NI, kMf = 2 * MI * NI;
+        static_assert(kLoads <= kMf && kReads <= kMf, "one load and one read per MFMA at most");
+        const typename PipeLoads<C>::Buf bufs = ld.buffers(a_tile, g_tile, u_tile);
+        const int64_t nmain = nk - (k_dim % C::BK == 0 ? 2 : 3);
+        constexpr int b = (KK - 1) & 1;
+        for (; kt < nmain; ++kt) {
+            uint16_t* cur = lds + (kt & 1) * C::kStageElems;
+            const uint16_t* nxt = lds + ((kt + 1) & 1) * C::kStageElems;
+#pragma unroll
+            for (int kk = 0; kk + 1 < KK; ++kk) {
+                read(cur, (kk + 1) & 1, kk + 1);
+                mfma(kk & 1);
+                interleave();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            wait_loads_but<0>();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            const int kq = lane / 32;
+#pragma unroll
+            for (int i = 0; i < kMf; ++i) {
+                const int mi = i / (2 * NI), ni = (i / 2) % NI;
+                if (i % 2 == 0)
+                    acc_g[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[b][mi], fg[b][ni], acc_g[mi][ni], 0, 0, 0);
+                else
+                    acc_u[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[b][mi], fu[b][ni], acc_u[mi][ni], 0, 0, 0);
+                if (i < kLoads) ld.issue_one(bufs, cur, kt + 2, i);
+                if (i < MI) {
+                    fa[0][i] = frag_swz<C::kCpr>(nxt, wm * (C::BM / C::WM) + i * 32 + lane % 32, kq);
+                } else if (i < kReads) {
+                    const int j = (i - MI) / 2;
+                    const uint16_t* w = nxt + C::kAElems + ((i - MI) % 2) * C::kWElems;
+                    const bf16x8 f = frag_swz<C::kCpr>(w, wn * (C::BN / C::WN) + j * 32 + lane % 32, kq);
+                    if ((i - MI) % 2 == 0)
+                        fg[0][j] = f;
+                    else
+                        fu[0][j] = f;
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep this order: MFMA, load, read
+            }
+        }
+    }
+    for (; kt < nk; ++kt) {
         uint16_t* cur = lds + (kt & 1) * C::kStageElems;
         uint16_t* nxt = lds + ((kt + 1) & 1) * C::kStageElems;
 #pragma unroll
@@ -380,7 +476,7 @@ enum class Epi { kSwiglu, kRouterBf16, kRouterF32 };
 // A grouped GEMM over rows grouped by expert: the reduction runs over k_dim
 // (hidden for gate_up, inter for the down projection); n_dim is the width of
 // each weight tensor's output (inter for gate_up, hidden for down).
-template <class C, Epi kEpi, bool kWriteX>
+template <class C, Epi kEpi, bool kWriteX, bool kBuf>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::OCC))) void grouped_gemm_kernel(
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w2,
     const int32_t* __restrict__ offs, const float* __restrict__ probs, void* __restrict__ out,
@@ -421,7 +517,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
             acc_u[mi][ni] = f32x16{};
         }
 
-    mainloop_pipe<C>(lds, a_tile, g_tile, u_tile, tr.rows, ncols1, ncols2 > 0 ? ncols2 : 1, k_dim, acc_g, acc_u);
+    mainloop_pipe<C, kBuf>(lds, a_tile, g_tile, u_tile, tr.rows, ncols1, ncols2 > 0 ? ncols2 : 1, k_dim, acc_g, acc_u);
     __syncthreads();  // all fragment reads done before the buffers become the staging tile
 
     uint16_t* stage = lds;
@@ -531,6 +627,26 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     }
 }
 
+// Largest reduction length for the buffer-form loads: every byte offset from a
+// tile's base, (BM - 1) rows plus a whole row of k_dim bf16 values, stays
+// below 2^31.
+template <class C>
+constexpr int64_t kBufMaxK = ((int64_t{1} << 31) - 1) / (2 * (C::BM + 1));
+
+template <class C, Epi kEpi, bool kWriteX>
+void launch_kernel(bool buf, int64_t grid, hipStream_t st, const uint16_t* a, const uint16_t* w1, const uint16_t* w2,
+                   const int32_t* offs, const float* probs, void* out, uint16_t* x_out, int64_t tokens, int64_t k_dim,
+                   int64_t n_dim, int64_t experts, float limit, int64_t n_tiles, int64_t n_blocks) {
+    if (buf)
+        hipLaunchKernelGGL((grouped_gemm_kernel<C, kEpi, kWriteX, true>), dim3(static_cast<unsigned>(grid)),
+                           dim3(C::kThreads), 0, st, a, w1, w2, offs, probs, out, x_out, tokens, k_dim, n_dim, experts,
+                           limit, n_tiles, n_blocks);
+    else
+        hipLaunchKernelGGL((grouped_gemm_kernel<C, kEpi, kWriteX, false>), dim3(static_cast<unsigned>(grid)),
+                           dim3(C::kThreads), 0, st, a, w1, w2, offs, probs, out, x_out, tokens, k_dim, n_dim, experts,
+                           limit, n_tiles, n_blocks);
+}
+
 template <class C, Epi kEpi>
 int launch_grouped(const uint16_t* a, const uint16_t* w1, const uint16_t* w2, const int32_t* offs,
                    const float* probs, void* out, uint16_t* x_out, int64_t tokens, int64_t k_dim, int64_t n_dim,
@@ -539,15 +655,14 @@ int launch_grouped(const uint16_t* a, const uint16_t* w1, const uint16_t* w2, co
     const int64_t grid = grouped_grid(tokens, n_dim, kEpi == Epi::kSwiglu ? C::BN : 2 * C::BN, experts, C::BM, &n_tiles,
                                          &n_blocks);
     if (grid == 0) return MOE_EPI_ERR_BAD_SHAPE;
+    const bool buf = k_dim <= kBufMaxK<C>;
     (void)hipGetLastError();
     if (kEpi == Epi::kSwiglu && x_out)
-        hipLaunchKernelGGL((grouped_gemm_kernel<C, kEpi, true>), dim3(static_cast<unsigned>(grid)), dim3(C::kThreads),
-                           0, st, a, w1, w2, offs, probs, out, x_out, tokens, k_dim, n_dim, experts, limit, n_tiles,
-                           n_blocks);
+        launch_kernel<C, kEpi, true>(buf, grid, st, a, w1, w2, offs, probs, out, x_out, tokens, k_dim, n_dim, experts,
+                                     limit, n_tiles, n_blocks);
     else
-        hipLaunchKernelGGL((grouped_gemm_kernel<C, kEpi, false>), dim3(static_cast<unsigned>(grid)),
-                           dim3(C::kThreads), 0, st, a, w1, w2, offs, probs, out, x_out, tokens, k_dim, n_dim, experts,
-                           limit, n_tiles, n_blocks);
+        launch_kernel<C, kEpi, false>(buf, grid, st, a, w1, w2, offs, probs, out, x_out, tokens, k_dim, n_dim, experts,
+                                      limit, n_tiles, n_blocks);
     return launch_status();
 }
 

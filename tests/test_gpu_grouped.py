@@ -143,3 +143,36 @@ def test_full_size_sampled_rows():
     y_o = oracle.swiglu_clamped_fwd(x[idx], d["probs"][idx], idx.size, w.inter, w.limit)
     sy = assert_bf16_parity(y[idx], y_o, f"{w.name} y")
     say(f"{w.name}: x {sx}, y exact {sy['exact']:.5f}")
+
+
+@pytest.mark.parametrize("k_dim", [4177920, 4178048])
+def test_reductions_beside_the_32_bit_load_offset_limit(k_dim):
+    """The main loop loads in buffer form (32-bit byte offsets from each tile's base)
+    while (BM + 1) * k_dim * 2 bytes stay below 2^31, i.e. k_dim <= 4178003 for 256-row
+    tiles, and in global form past that. 257 tokens in two row tiles put the largest
+    offsets just below and just above the limit. Inputs are built on the device:
+    a[t, h] = 1 where h = t (mod 7), else 0, and all weights 1, so every gate and up
+    output is the count of such h, exact in fp32 (below 2^24) and in bf16 after
+    rounding; y is checked against the oracle's forward of the kernel's own x."""
+    tokens, inter, experts, L = 257, 8, 1, 7.0
+    say(f"k_dim {k_dim}: device inputs ({tokens * k_dim * 2 / 2**30:.2f} GiB of activations)")
+    h = torch.arange(k_dim, device="cuda") % 7
+    a = (h[None, :] == (torch.arange(tokens, device="cuda") % 7)[:, None]).to(torch.bfloat16)
+    del h
+    w = torch.ones((experts, inter, k_dim), dtype=torch.bfloat16, device="cuda")
+    offs = torch.tensor([tokens], dtype=torch.int32, device="cuda")
+    p = torch.linspace(0.1, 1.0, tokens, device="cuda")
+    y = torch.empty((tokens, inter), dtype=torch.bfloat16, device="cuda")
+    x = torch.empty((tokens, 2 * inter), dtype=torch.bfloat16, device="cuda")
+    epi.grouped_gate_up_swiglu_fwd(a, w, w, offs, p, y, x, L)
+    torch.cuda.synchronize()
+    del a, w
+    t = np.arange(tokens)
+    counts = (k_dim - 1 - t % 7) // 7 + 1  # h in [0, k_dim) with h = t (mod 7)
+    want = (counts.astype(np.float32).view(np.uint32) + 0x7FFF + ((counts.astype(np.float32).view(np.uint32) >> 16) & 1)) >> 16
+    xb = to_host_bits(x)
+    assert np.array_equal(xb[:, :inter], np.repeat(want.astype(np.uint16)[:, None], inter, 1)), "gate sums"
+    assert np.array_equal(xb[:, inter:], np.repeat(want.astype(np.uint16)[:, None], inter, 1)), "up sums"
+    y_o = oracle.swiglu_clamped_fwd(xb, p.cpu().numpy(), tokens, inter, L)
+    assert_bf16_parity(to_host_bits(y), y_o, f"k_dim {k_dim} y")
+    say(f"k_dim {k_dim}: exact sums, y within the bar")
