@@ -87,8 +87,9 @@
 // copies before the interleave: MFMAs, barriers and epilogue alone 1677, plus
 // the fragment reads 1475, plus loads that all hit L2 1198, as launched 1100;
 // the loads not waited for at the barrier: no change. The shader clock averages about
-// 1.74 GHz in this kernel (busy cycles per XCD over the dispatch time), so
-// 2.5 PFLOP/s at 2.4 GHz is about 1.81 PFLOP/s at the clock it runs at.
+// 1.58 GHz in this kernel (busy cycles per XCD over the dispatch time; 1.74
+// before the loads were interleaved: the part is power-limited here), so
+// 2.5 PFLOP/s at 2.4 GHz is about 1.65 PFLOP/s at the clock it runs at.
 #include "epi_common.h"
 #include "grouped_map.h"
 #include "swiglu_math.h"
