@@ -25,9 +25,14 @@ Prints one JSON line. Options:
   --no-grad-probs    backward without the probability gradient (probabilities
                      that carry no gradient; the router then does not read x)
   --no-cpu-baseline  skip the oracle timing on the host
-  --flush-cache      SwiGLU / router: a 1 GiB write before every launch, outside
-                     its events, evicts L2 and the 256 MB Infinity Cache; the
-                     step time is then the sum of the two kernels' event times
+  --warm             SwiGLU / router: launch each kernel straight after the
+                     previous one. The default is a 1 GiB write before every
+                     launch, outside its events, which evicts L2 and the 256 MB
+                     Infinity Cache, so a workload smaller than them is not
+                     served from them; the step time is then the sum of the
+                     two kernels' event times
+  --no-copy-ceiling  skip timing the 1 GiB device copy whose bandwidth the
+                     SwiGLU / router lines also report a fraction of
   --all              the four SwiGLU workloads and the router workload in
                      turn, one JSON line each (the default is the headline
                      workload alone, one line)
@@ -89,8 +94,10 @@ def parse_args():
     ap.add_argument("--cpu-threads", type=int, default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-x", action="store_true")
-    ap.add_argument("--flush-cache", action="store_true",
-                    help="SwiGLU / router: evict L2 and the Infinity Cache (1 GiB write) before every launch")
+    ap.add_argument("--warm", action="store_true",
+                    help="SwiGLU / router: no cache flush between launches (default: a 1 GiB write before each)")
+    ap.add_argument("--no-copy-ceiling", action="store_true",
+                    help="SwiGLU / router: do not time the 1 GiB device copy (the box's copy ceiling)")
     ap.add_argument("--all", action="store_true",
                     help="every SwiGLU and router workload in turn, one JSON line each")
     return ap.parse_args()
@@ -131,6 +138,9 @@ def kernel_source_digest(op: str) -> str:
 
 
 PROFILE_FOR = {"swiglu": "swiglu_clamped", "router": "router_weight_mul"}
+
+# SwiGLU workloads up to this many rows also report the oracle on one thread
+SINGLE_THREAD_ROWS = 8192
 
 
 def op_of(workload) -> str:
@@ -174,6 +184,33 @@ def load_traffic(kernel: str, workload) -> float | None:
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def copy_ceiling(steps: int = 20) -> dict:
+    """Bandwidth of a plain 1 GiB device-to-device copy on this machine (torch's
+    copy_, carried out by the HIP runtime's copy kernel), bytes read plus bytes
+    written over the average launch time: what a kernel that only moves data
+    sustains here, next to the 8 TB/s peak."""
+    import torch
+    n = 1 << 29  # 2**29 bf16 = 1 GiB
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    avg = sum(a.elapsed_time(b) for a, b in evs) / steps
+    gbs = 2 * n * 2 / (avg * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"GB/s": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS,
+            "how": f"1 GiB device-to-device copy (torch copy_), read + written bytes over the average of {steps} "
+                   "launches"}
 
 
 def copy_calibration(args):
@@ -224,14 +261,18 @@ def main():
         return down_main(args, DOWN_WORKLOADS[args.workload])
     if args.workload in COMBINE_WORKLOADS:
         return combine_main(args, COMBINE_WORKLOADS[args.workload])
+    ceiling = None
+    if not args.no_copy_ceiling:
+        print("[bench] timing a 1 GiB device copy (the copy ceiling)", file=sys.stderr, flush=True)
+        ceiling = copy_ceiling()
     if args.all:
         for name in WORKLOADS:  # the five SwiGLU / router workloads, one line each
-            epilogue_main(args, WORKLOADS[name])
+            epilogue_main(args, WORKLOADS[name], ceiling)
         return None
-    return epilogue_main(args, WORKLOADS[args.workload or HEADLINE])
+    return epilogue_main(args, WORKLOADS[args.workload or HEADLINE], ceiling)
 
 
-def epilogue_main(args, w):
+def epilogue_main(args, w, ceiling=None):
     """One clamped-SwiGLU or router-weight-multiply workload: forward + backward per step."""
     import numpy as np
     import torch
@@ -280,10 +321,10 @@ def epilogue_main(args, w):
 
     E = lambda: torch.cuda.Event(enable_timing=True)
     evs = [(E(), E(), E(), E()) for _ in range(args.steps)]
-    # --flush-cache: a 1 GiB write before each launch evicts L2 and the 256 MB
+    # unless --warm: a 1 GiB write before each launch evicts L2 and the 256 MB
     # Infinity Cache, so that a workload smaller than them is not served from
     # them; the flushes lie outside the kernels' events
-    scratch = torch.empty((1 << 28,), dtype=torch.float32, device=dev) if args.flush_cache else None
+    scratch = None if args.warm else torch.empty((1 << 28,), dtype=torch.float32, device=dev)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -311,8 +352,11 @@ def epilogue_main(args, w):
     def kstats(name, nbytes, ms):
         avg = float(ms.mean())
         gbs = nbytes / (avg * 1e-3) / 1e9
-        return {"avg_us": avg * 1e3, "median_us": float(np.median(ms)) * 1e3, "min_us": float(ms.min()) * 1e3,
-                "algorithmic_bytes": nbytes, "GB/s": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS}
+        k = {"avg_us": avg * 1e3, "median_us": float(np.median(ms)) * 1e3, "min_us": float(ms.min()) * 1e3,
+             "algorithmic_bytes": nbytes, "GB/s": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS}
+        if ceiling is not None:
+            k["frac_of_copy"] = gbs / ceiling["GB/s"]
+        return k
 
     kernels = {names[0]: kstats(names[0], fwd_b, fwd_ms), names[1]: kstats(names[1], bwd_b, bwd_ms)}
     # Counter traffic is taken for the bf16, with-gradient launch only.
@@ -327,7 +371,7 @@ def epilogue_main(args, w):
                 "unit": "GB/s", "frac": kernels[dom]["GB/s"] / PEAK_HBM_GBS, "traffic": traffic,
                 "algorithmic_bytes_per_launch": kernels[dom]["algorithmic_bytes"]}
 
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
         import oracle
         threads = args.cpu_threads or oracle.default_threads()
@@ -335,7 +379,7 @@ def epilogue_main(args, w):
         print(f"[bench] oracle on the host ({threads} threads): whole-workload passes for >= {args.cpu_seconds:g} s",
               file=sys.stderr, flush=True)
 
-        def oracle_pass():
+        def oracle_pass():  # reads `threads` when called
             if w.op == "swiglu":
                 oracle.swiglu_clamped_fwd_typed(d["x"], code[dt], d["probs"], rows, cols, w.limit, threads=threads)
                 oracle.swiglu_clamped_bwd_typed(d["x"], code[dt], d["probs"], d["grad_out"], rows, cols, w.limit,
@@ -355,6 +399,15 @@ def epilogue_main(args, w):
                 break
         cpu = {"value": passes * (fwd_b + bwd_b) / ct / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
                "sample": f"{passes} passes over the whole workload ({rows} rows, forward + backward), {ct:.1f} s"}
+        if w.op == "swiglu" and rows <= SINGLE_THREAD_ROWS:
+            # the small workloads also on one host thread
+            print(f"[bench] oracle on one host thread: whole-workload passes for >= {args.cpu_seconds / 4:g} s",
+                  file=sys.stderr, flush=True)
+            threads = 1
+            passes, ct = oracle_timed(oracle_pass, args.cpu_seconds / 4)
+            cpu1 = {"value": passes * (fwd_b + bwd_b) / ct / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                    "sample": f"{passes} passes over the whole workload ({rows} rows, forward + backward), "
+                              f"{ct:.1f} s"}
 
     headline = w.name == HEADLINE and not variant
     line = {
@@ -376,12 +429,17 @@ def epilogue_main(args, w):
                    ("inter" if w.op == "swiglu" else "hidden"): cols,
                    "limit": w.limit, "storage": dt, "output": od, "grad_probs": want_gp,
                    "io": f"{dt} tensors, fp32 probs; fp32 arithmetic", "bytes_per_step": fwd_b + bwd_b,
-                   "caches": "flushed before every launch" if args.flush_cache else "warm from the previous launch"},
+                   "caches": "warm from the previous launch" if args.warm else
+                   "flushed before every launch (1 GiB write outside the events)"},
         "frac_of_peak": value / PEAK_HBM_GBS,
+        "frac_of_copy": None if ceiling is None else value / ceiling["GB/s"],
+        "copy_ceiling": ceiling,
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if cpu1 is not None:
+        line["cpu_baseline_1thread"] = cpu1
     print(json.dumps(line), flush=True)
 
 

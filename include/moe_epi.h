@@ -43,8 +43,8 @@ typedef enum moe_epi_status {
     MOE_EPI_ERR_BAD_SHAPE = 2,    /* rows < 0, inter/hidden <= 0, or a byte size overflows   */
     MOE_EPI_ERR_BAD_LIMIT = 3,    /* limit is not finite or not > 0                          */
     MOE_EPI_ERR_ALIAS = 4,        /* an output overlaps an input or another output           */
-    MOE_EPI_ERR_MISALIGNED = 5,   /* a pointer is not aligned to its element size            */
-    MOE_EPI_ERR_LAUNCH = 6,       /* the HIP runtime reported an error at kernel launch      */
+    MOE_EPI_ERR_LAUNCH = 5,       /* the HIP runtime reported an error at kernel launch      */
+    MOE_EPI_ERR_MISALIGNED = 6,   /* a pointer is not aligned to its element size            */
     MOE_EPI_ERR_BAD_DTYPE = 7     /* a dtype code is not one of moe_epi_dtype                */
 } moe_epi_status;
 

@@ -34,8 +34,8 @@ STATUS = {
     2: "MOE_EPI_ERR_BAD_SHAPE",
     3: "MOE_EPI_ERR_BAD_LIMIT",
     4: "MOE_EPI_ERR_ALIAS",
-    5: "MOE_EPI_ERR_MISALIGNED",
-    6: "MOE_EPI_ERR_LAUNCH",
+    5: "MOE_EPI_ERR_LAUNCH",
+    6: "MOE_EPI_ERR_MISALIGNED",
     7: "MOE_EPI_ERR_BAD_DTYPE",
 }
 

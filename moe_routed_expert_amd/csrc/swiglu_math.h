@@ -14,9 +14,16 @@
 namespace moe_epi {
 
 // sigma(z) = 1 / (1 + e^-z) with e^-z = 2^(-z * log2(e)).
+// v_rcp_f32 returns no subnormal results: for z in about (-88.7, -87.3] the
+// true 1/(1 + e) lies below 2^-126 and would come back as 0, turning silu(z)
+// (a normal number there, z times that subnormal) into a zero. So the
+// reciprocal is taken of (1 + e) * 2^-32, which keeps it normal for every
+// finite 1 + e, and scaled back by 2^-32: both scalings are exact above
+// 2^-126, and below it the final multiply rounds into the subnormal range as
+// IEEE division would (the kernels run with fp32 subnormals enabled).
 __device__ __forceinline__ float sigmoid_f32(float z) {
     const float e = __builtin_amdgcn_exp2f(z * -1.4426950408889634f);
-    return __builtin_amdgcn_rcpf(1.0f + e);
+    return __builtin_amdgcn_rcpf((1.0f + e) * 0x1p-32f) * 0x1p-32f;
 }
 
 // clamp(gate, max=L): a comparison with NaN is false, so NaN passes through.

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # case that passed validation would launch on fake addresses), so skip there.
 pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0, reason="host-only checks; a GPU is visible")
 
-OK, NULLP, SHAPE, LIMIT, ALIAS, MISAL, LAUNCH, DTYPE = range(8)
+OK, NULLP, SHAPE, LIMIT, ALIAS, LAUNCH, MISAL, DTYPE = range(8)
 
 
 @pytest.fixture(scope="module")
@@ -54,6 +54,36 @@ def test_status_strings(L):
         assert s and s != "unknown status"
     assert binding.describe(99) == "unknown status"
     assert binding.describe(0) == "success"
+
+
+# The status codes as the boundary specifies them: the first six in the order
+# of the specification (MOE_EPI_ERR_LAUNCH = 5), the two this library adds
+# appended after them, so a caller written to the first six reads every code
+# the same way.
+SPEC_STATUS = {
+    "MOE_EPI_SUCCESS": 0,
+    "MOE_EPI_ERR_NULL_POINTER": 1,
+    "MOE_EPI_ERR_BAD_SHAPE": 2,
+    "MOE_EPI_ERR_BAD_LIMIT": 3,
+    "MOE_EPI_ERR_ALIAS": 4,
+    "MOE_EPI_ERR_LAUNCH": 5,
+    "MOE_EPI_ERR_MISALIGNED": 6,
+    "MOE_EPI_ERR_BAD_DTYPE": 7,
+}
+
+
+def test_status_code_values_pinned(L):
+    text = open(os.path.join(ROOT, "include", "moe_epi.h")).read()
+    body = re.search(r"typedef enum moe_epi_status \{(.*?)\} moe_epi_status;", text, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    header = {m.group(1): int(m.group(2)) for m in re.finditer(r"(MOE_EPI_\w+)\s*=\s*(\d+)", body)}
+    assert header == SPEC_STATUS
+    assert binding.STATUS == {v: k for k, v in SPEC_STATUS.items()}
+    # the library's own strings say what each code means
+    assert "launch" in binding.describe(5)
+    assert "aligned" in binding.describe(6)
+    assert "dtype" in binding.describe(7)
+    assert "NULL" in binding.describe(1) or "null" in binding.describe(1)
 
 
 # fake, never dereferenced device addresses (validation fails before any use)
