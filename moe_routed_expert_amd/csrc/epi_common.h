@@ -120,6 +120,20 @@ __device__ __forceinline__ int group_in_block() {
         return g;
 }
 
+// ---- aligned row loads ---------------------------------------------------------
+//
+// A barrier of the whole block before its wavefronts issue their row loads, so
+// that the block's requests (its rows are contiguous in memory) reach the
+// memory system together rather than spread over the time its wavefronts
+// took to start. Every wavefront of the block must call it the same number of
+// times, rows past the end included. Measured on MI355X with the caches
+// flushed before every launch: the clamped SwiGLU forward at 131072 x 2048
+// bf16 went from 80.8-81.0% to 85.1-85.5% of HBM peak with three 192-lane
+// rows per block, the backward from 78.6% to 82.8-83.1%; a wait for the
+// row's probability before the loads did the same. Blocks of 256-lane rows
+// gained nothing from it.
+__device__ __forceinline__ void align_block_loads() { __syncthreads(); }
+
 // ---- occupancy ------------------------------------------------------------------
 //
 // Waves per SIMD that let two blocks of B threads share a CU: a block's waves

@@ -30,7 +30,9 @@ constexpr int kBlock = 256;
 // B threads per block. The row loop advances whole blocks so that every thread
 // of a block runs the same iterations (row_sum may hold a barrier). TX is the
 // dtype of x and grad_x, TO that of out and grad_out.
-template <int TX, int TO, int G, int V, int B>
+// kAlign: the block's wavefronts meet at a barrier before any of them issues
+// its row loads (align_block_loads, epi_common.h).
+template <int TX, int TO, int G, int V, int B, bool kAlign>
 __global__ __launch_bounds__(B) void router_weight_mul_fwd_kernel(const void* __restrict__ x,
                                                                   const float* __restrict__ probs,
                                                                   void* __restrict__ out, int64_t rows,
@@ -44,10 +46,11 @@ __global__ __launch_bounds__(B) void router_weight_mul_fwd_kernel(const void* __
     for (int64_t rb = static_cast<int64_t>(blockIdx.x) * kRows; rb < rows;
          rb += static_cast<int64_t>(gridDim.x) * kRows) {
         const int64_t r = rb + group_in_block<G>();
+        const float p = r < rows ? probs[r] : 0.0f;
+        if constexpr (kAlign) align_block_loads();
         if (r >= rows) continue;
         const void* xr = row_at<TX>(x, r * hidden);
         void* outr = row_at<TO>(out, r * hidden);
-        const float p = probs[r];
         for (uint32_t c0 = lane; c0 < nvec; c0 += G * V) {
             typename EX::Raw v[V];
             Quads q[V];
@@ -70,7 +73,7 @@ __global__ __launch_bounds__(B) void router_weight_mul_fwd_kernel(const void* __
     }
 }
 
-template <int TX, int TO, int G, int V, int B, bool kGradProbs>
+template <int TX, int TO, int G, int V, int B, bool kGradProbs, bool kAlign>
 __global__ __launch_bounds__(B) __attribute__((amdgpu_waves_per_eu(waves_for_two_blocks(B)))) void
 router_weight_mul_bwd_kernel(const void* __restrict__ grad_out, const void* __restrict__ x,
                              const float* __restrict__ probs, void* __restrict__ grad_x,
@@ -86,11 +89,12 @@ router_weight_mul_bwd_kernel(const void* __restrict__ grad_out, const void* __re
          rb += static_cast<int64_t>(gridDim.x) * kRows) {
         const int64_t r = rb + group_in_block<G>();
         float acc = 0.0f;
+        const float p = r < rows ? probs[r] : 0.0f;
+        if constexpr (kAlign) align_block_loads();
         if (r < rows) {
             const void* gor = row_at<TO>(grad_out, r * hidden);
             const void* xr = kGradProbs ? row_at<TX>(x, r * hidden) : nullptr;
             void* gxr = row_at<TX>(grad_x, r * hidden);
-            const float p = probs[r];
             for (uint32_t c0 = lane; c0 < nvec; c0 += G * V) {
                 typename EO::Raw g[V];
                 typename EX::Raw xv[V];
@@ -191,22 +195,22 @@ constexpr Cls cls_of() {
     return TX == MOE_EPI_F32 ? Cls::k32 : (TO == MOE_EPI_F32 ? Cls::kMixed : Cls::k16);
 }
 
-template <int TX, int TO, int G, int V, int B>
+template <int TX, int TO, int G, int V, int B, bool kAlign = false>
 void launch_fwd(const void* x, const float* probs, void* out, int64_t rows, int64_t hidden, hipStream_t st) {
-    hipLaunchKernelGGL((router_weight_mul_fwd_kernel<TX, TO, G, V, B>), dim3(grid_for_rows(rows, B / G)), dim3(B), 0,
-                       st, x, probs, out, rows, hidden);
+    hipLaunchKernelGGL((router_weight_mul_fwd_kernel<TX, TO, G, V, B, kAlign>), dim3(grid_for_rows(rows, B / G)),
+                       dim3(B), 0, st, x, probs, out, rows, hidden);
 }
 
-template <int TX, int TO, int G, int V, int B>
+template <int TX, int TO, int G, int V, int B, bool kAlign = false>
 void launch_bwd(const void* go, const void* x, const float* probs, void* gx, float* gp, int64_t rows, int64_t hidden,
                 hipStream_t st) {
     const dim3 grid(grid_for_rows(rows, B / G));
     if (gp)
-        hipLaunchKernelGGL((router_weight_mul_bwd_kernel<TX, TO, G, V, B, true>), grid, dim3(B), 0, st, go, x, probs,
-                           gx, gp, rows, hidden);
+        hipLaunchKernelGGL((router_weight_mul_bwd_kernel<TX, TO, G, V, B, true, kAlign>), grid, dim3(B), 0, st, go, x,
+                           probs, gx, gp, rows, hidden);
     else
-        hipLaunchKernelGGL((router_weight_mul_bwd_kernel<TX, TO, G, V, B, false>), grid, dim3(B), 0, st, go, x, probs,
-                           gx, gp, rows, hidden);
+        hipLaunchKernelGGL((router_weight_mul_bwd_kernel<TX, TO, G, V, B, false, kAlign>), grid, dim3(B), 0, st, go, x,
+                           probs, gx, gp, rows, hidden);
 }
 
 template <int TX, int TO>
@@ -227,7 +231,10 @@ void dispatch_fwd(const void* x, const float* probs, void* out, int64_t rows, in
         if constexpr (c == Cls::k16) {
             if (nvec <= 256) return launch_fwd<TX, TO, 192, 1, 192>(x, probs, out, rows, hidden, st);
             if (nvec <= 512) return launch_fwd<TX, TO, 192, 2, 384>(x, probs, out, rows, hidden, st);
-            return launch_fwd<TX, TO, 320, 2, 320>(x, probs, out, rows, hidden, st);
+            // 513-1024 vectors: 320 lanes of two vectors a pass, three rows per
+            // block, aligned (align_block_loads): at 7168 columns 79.7% of HBM
+            // peak against 76.3% for one unaligned row per block
+            return launch_fwd<TX, TO, 320, 2, 960, true>(x, probs, out, rows, hidden, st);
         } else if constexpr (c == Cls::kMixed) {
             if (nvec <= 256) return launch_fwd<TX, TO, 640, 1, 640>(x, probs, out, rows, hidden, st);
             if (nvec <= 512) return launch_fwd<TX, TO, 896, 2, 896>(x, probs, out, rows, hidden, st);
@@ -260,7 +267,9 @@ void dispatch_bwd(const void* go, const void* x, const float* probs, void* gx, f
         if constexpr (c == Cls::k16) {
             if (nvec <= 256) return launch_bwd<TX, TO, 256, 2, 512>(go, x, probs, gx, gp, rows, hidden, st);
             if (nvec <= 512) return launch_bwd<TX, TO, 512, 2, 1024>(go, x, probs, gx, gp, rows, hidden, st);
-            return launch_bwd<TX, TO, 448, 2, 896>(go, x, probs, gx, gp, rows, hidden, st);
+            // 513-1024 vectors, aligned (align_block_loads): at 7168 columns
+            // 81.3% of HBM peak against 77.7% unaligned
+            return launch_bwd<TX, TO, 448, 2, 896, true>(go, x, probs, gx, gp, rows, hidden, st);
         } else if constexpr (c == Cls::kMixed) {
             if (nvec <= 256) return launch_bwd<TX, TO, 320, 1, 640>(go, x, probs, gx, gp, rows, hidden, st);
             if (nvec <= 512) return launch_bwd<TX, TO, 512, 2, 1024>(go, x, probs, gx, gp, rows, hidden, st);

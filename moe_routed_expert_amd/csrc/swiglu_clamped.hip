@@ -15,11 +15,16 @@
 //     l, l + G, ... of the row (16 bytes for 16-bit types), so each
 //     wavefront-wide access is 1 KiB contiguous in gate, up, grad_y and the
 //     outputs. All V vectors of a pass are loaded (gate, then up, then grad_y)
-//     before any math. At inter = 2048 the forward spreads a row over 4
-//     wavefronts (1 vector per lane) and the backward over 2 (2 vectors per
-//     lane): the shapes that sustained the most bandwidth on MI355X among 1-4
-//     wavefronts per row, 64-1024 thread blocks, persistent grids and register
-//     double-buffering across rows.
+//     before any math. At inter = 2048 (256 vectors) both kernels spread a row
+//     over 3 wavefronts (192 lanes: the first wavefront takes vectors 0-63
+//     and 192-255, the other two one vector per lane; the backward loads the
+//     first wavefront's two vectors together) and put three rows in a
+//     576-lane block: the shapes that sustained the most bandwidth on MI355X,
+//     with the caches flushed before every launch, among 1-4 wavefronts per
+//     row, 1-5 rows per block, 64-1024 thread blocks, block orders that give
+//     each XCD contiguous runs of rows, persistent grids and register
+//     double-buffering across rows (the launchers below give the measured
+//     alternatives).
 //   * The probability gradient is a per-lane fp32 register accumulator,
 //     reduced with cross-lane shuffles within each wavefront and, when a row
 //     spans several wavefronts, through a few LDS slots in a fixed order.
@@ -87,7 +92,9 @@ __device__ __forceinline__ void bwd_vec(typename Elem<T>::Raw g, typename Elem<T
 // blocks, so every thread of a block runs the same iterations (row_sum may
 // hold a barrier). Element offsets below are in elements of T.
 
-template <int T, int G, int V, int B>
+// kAlign: the block's wavefronts meet at a barrier before any of them issues
+// its row loads (align_block_loads, epi_common.h).
+template <int T, int G, int V, int B, bool kAlign>
 __global__ __launch_bounds__(B) void swiglu_clamped_fwd_kernel(const void* __restrict__ x,
                                                                const float* __restrict__ probs, void* __restrict__ y,
                                                                int64_t rows, int64_t inter, float L) {
@@ -99,11 +106,12 @@ __global__ __launch_bounds__(B) void swiglu_clamped_fwd_kernel(const void* __res
     for (int64_t rb = static_cast<int64_t>(blockIdx.x) * kRows; rb < rows;
          rb += static_cast<int64_t>(gridDim.x) * kRows) {
         const int64_t r = rb + group_in_block<G>();
+        const float p = r < rows ? probs[r] : 0.0f;
+        if constexpr (kAlign) align_block_loads();
         if (r >= rows) continue;
         const void* xg = row_at<T>(x, r * 2 * inter);
         const void* xu = row_at<T>(x, r * 2 * inter + inter);
         void* yr = row_at<T>(y, r * inter);
-        const float p = probs[r];
         for (uint32_t c0 = lane; c0 < nvec; c0 += G * V) {
             typename E::Raw g[V], u[V];
             Quads q[V];
@@ -122,7 +130,7 @@ __global__ __launch_bounds__(B) void swiglu_clamped_fwd_kernel(const void* __res
     }
 }
 
-template <int T, int G, int V, int B, bool kGradProbs>
+template <int T, int G, int V, int B, bool kGradProbs, bool kAlign>
 __global__ __launch_bounds__(B) __attribute__((amdgpu_waves_per_eu(waves_for_two_blocks(B)))) void
 swiglu_clamped_bwd_kernel(const void* __restrict__ x, const float* __restrict__ probs, const void* __restrict__ grad_y,
                           void* __restrict__ grad_x, float* __restrict__ grad_probs, int64_t rows, int64_t inter,
@@ -137,13 +145,14 @@ swiglu_clamped_bwd_kernel(const void* __restrict__ x, const float* __restrict__ 
          rb += static_cast<int64_t>(gridDim.x) * kRows) {
         const int64_t r = rb + group_in_block<G>();
         float acc = 0.0f;
+        const float p = r < rows ? probs[r] : 0.0f;
+        if constexpr (kAlign) align_block_loads();
         if (r < rows) {
             const void* xg = row_at<T>(x, r * 2 * inter);
             const void* xu = row_at<T>(x, r * 2 * inter + inter);
             const void* gyr = row_at<T>(grad_y, r * inter);
             void* gxg = row_at<T>(grad_x, r * 2 * inter);
             void* gxu = row_at<T>(grad_x, r * 2 * inter + inter);
-            const float p = probs[r];
             for (uint32_t c0 = lane; c0 < nvec; c0 += G * V) {
                 typename E::Raw g[V], u[V], gy[V];
                 Quads q[V];
@@ -241,22 +250,22 @@ __global__ __launch_bounds__(kBwdBlock) void swiglu_clamped_bwd_scalar_kernel(
 // under 64 vectors, up to 4 wavefronts between 64 and 191). Rows wider than a
 // shape covers take several passes.
 
-template <int T, int G, int V, int B>
+template <int T, int G, int V, int B, bool kAlign = false>
 void launch_fwd(const void* x, const float* probs, void* y, int64_t rows, int64_t inter, float L, hipStream_t st) {
-    hipLaunchKernelGGL((swiglu_clamped_fwd_kernel<T, G, V, B>), dim3(grid_for_rows(rows, B / G)), dim3(B), 0, st, x,
-                       probs, y, rows, inter, L);
+    hipLaunchKernelGGL((swiglu_clamped_fwd_kernel<T, G, V, B, kAlign>), dim3(grid_for_rows(rows, B / G)), dim3(B), 0,
+                       st, x, probs, y, rows, inter, L);
 }
 
-template <int T, int G, int V, int B>
+template <int T, int G, int V, int B, bool kAlign = false>
 void launch_bwd(const void* x, const float* probs, const void* gy, void* gx, float* gp, int64_t rows, int64_t inter,
                 float L, hipStream_t st) {
     const dim3 grid(grid_for_rows(rows, B / G));
     if (gp)
-        hipLaunchKernelGGL((swiglu_clamped_bwd_kernel<T, G, V, B, true>), grid, dim3(B), 0, st, x, probs, gy, gx, gp,
-                           rows, inter, L);
+        hipLaunchKernelGGL((swiglu_clamped_bwd_kernel<T, G, V, B, true, kAlign>), grid, dim3(B), 0, st, x, probs, gy, gx,
+                           gp, rows, inter, L);
     else
-        hipLaunchKernelGGL((swiglu_clamped_bwd_kernel<T, G, V, B, false>), grid, dim3(B), 0, st, x, probs, gy, gx, gp,
-                           rows, inter, L);
+        hipLaunchKernelGGL((swiglu_clamped_bwd_kernel<T, G, V, B, false, kAlign>), grid, dim3(B), 0, st, x, probs, gy,
+                           gx, gp, rows, inter, L);
 }
 
 template <int T>
@@ -276,10 +285,18 @@ void dispatch_fwd(const void* x, const float* probs, void* y, int64_t rows, int6
         if (nvec <= 512) return launch_fwd<T, 448, 4, 448>(x, probs, y, rows, inter, L, st);
         return launch_fwd<T, 384, 1, 384>(x, probs, y, rows, inter, L, st);
     } else {
-        if (nvec == 192) return launch_fwd<T, 256, 1, 512>(x, probs, y, rows, inter, L, st);
-        // a full 256-vector row (inter 2048): four rows per 1024-lane block ran at
-        // 81.7% of HBM peak against 80.5% with one row per block (bf16 and fp16 alike)
-        if (nvec == 256) return launch_fwd<T, 256, 1, 1024>(x, probs, y, rows, inter, L, st);
+        // 192 vectors (inter 1536): 128 lanes per row (the first wavefront
+        // takes two vectors per lane), three rows per block, aligned: 81.2% of
+        // HBM peak against 79.5% for two unaligned 256-lane rows per block
+        if (nvec == 192) return launch_fwd<T, 128, 1, 384, true>(x, probs, y, rows, inter, L, st);
+        // a full 256-vector row (inter 2048): 192 lanes per row (the first
+        // wavefront takes vectors 0-63 and 192-255, the others one vector per
+        // lane), three rows per 576-lane block, the block aligned before its
+        // loads: 85.1-85.5% of HBM peak (caches flushed before every launch),
+        // against 80.8-81.0% for the same shape unaligned, 79.8-80.6% for
+        // four 256-lane rows per 1024-lane block (aligned or not), 83.7-84.2%
+        // for two aligned 192-lane rows
+        if (nvec == 256) return launch_fwd<T, 192, 1, 576, true>(x, probs, y, rows, inter, L, st);
         // 193-255 vectors: 192 lanes per row, two rows per block (224 vectors: 82.4%
         // against 79.7% for 256 lanes, one row; 193 vectors: the same within 0.5%)
         if (nvec < 256) return launch_fwd<T, 192, 1, 384>(x, probs, y, rows, inter, L, st);
@@ -306,7 +323,15 @@ void dispatch_bwd(const void* x, const float* probs, const void* gy, void* gx, f
         if (nvec <= 512) return launch_bwd<T, 640, 2, 640>(x, probs, gy, gx, gp, rows, inter, L, st);
         return launch_bwd<T, 512, 1, 1024>(x, probs, gy, gx, gp, rows, inter, L, st);
     } else {
-        if (nvec == 192) return launch_bwd<T, 256, 1, 512>(x, probs, gy, gx, gp, rows, inter, L, st);
+        // 192 vectors (inter 1536): one vector per lane of 192, three rows per
+        // block, aligned: 82.2% of HBM peak against 78.3% for two unaligned
+        // 256-lane rows per block
+        if (nvec == 192) return launch_bwd<T, 192, 1, 576, true>(x, probs, gy, gx, gp, rows, inter, L, st);
+        // 256 vectors (inter 2048): three 192-lane rows per block, aligned
+        // before the loads: 82.8-83.1% of HBM peak, against 78.6% unaligned,
+        // 81.1-82.0% with the first wavefront's two vectors loaded together,
+        // 79.6-80.5% for two 192-lane rows (aligned or not)
+        if (nvec == 256) return launch_bwd<T, 192, 1, 576, true>(x, probs, gy, gx, gp, rows, inter, L, st);
         if (nvec <= 256) return launch_bwd<T, 192, 1, 384>(x, probs, gy, gx, gp, rows, inter, L, st);
         if (nvec <= 512) return launch_bwd<T, 448, 1, 448>(x, probs, gy, gx, gp, rows, inter, L, st);
         return launch_bwd<T, 512, 2, 512>(x, probs, gy, gx, gp, rows, inter, L, st);
