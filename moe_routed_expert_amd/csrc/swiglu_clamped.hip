@@ -281,22 +281,37 @@ void dispatch_fwd(const void* x, const float* probs, void* y, int64_t rows, int6
     if (nvec == 64) return launch_fwd<T, 64, 1, 256>(x, probs, y, rows, inter, L, st);
     if (nvec <= 128) return launch_fwd<T, 128, 1, 256>(x, probs, y, rows, inter, L, st);
     if (nvec < 192) return launch_fwd<T, 256, 1, 256>(x, probs, y, rows, inter, L, st);
+    // At the widths of the workloads (192 and 256 vectors) the shapes come from
+    // a second sweep, per dtype, with the option of aligned row loads
+    // (align_block_loads, epi_common.h): the alignment helped bfloat16 and
+    // float32 and hurt float16 there, so each choice below holds only for the
+    // dtype it was measured on.
     if constexpr (T == MOE_EPI_F32) {
+        // 256 vectors, aligned: 86.0% of HBM peak against 78.3% unaligned
+        if (nvec == 256) return launch_fwd<T, 448, 4, 448, true>(x, probs, y, rows, inter, L, st);
         if (nvec <= 512) return launch_fwd<T, 448, 4, 448>(x, probs, y, rows, inter, L, st);
         return launch_fwd<T, 384, 1, 384>(x, probs, y, rows, inter, L, st);
     } else {
-        // 192 vectors (inter 1536): 128 lanes per row (the first wavefront
-        // takes two vectors per lane), three rows per block, aligned: 81.2% of
-        // HBM peak against 79.5% for two unaligned 256-lane rows per block
-        if (nvec == 192) return launch_fwd<T, 128, 1, 384, true>(x, probs, y, rows, inter, L, st);
+        // 192 vectors (inter 1536), bfloat16: 128 lanes per row (the first
+        // wavefront takes two vectors per lane), three rows per block,
+        // aligned: 81.2% of HBM peak against 79.5% for two unaligned 256-lane
+        // rows per block (the shape float16 keeps)
+        if (nvec == 192) {
+            if constexpr (T == MOE_EPI_BF16) return launch_fwd<T, 128, 1, 384, true>(x, probs, y, rows, inter, L, st);
+            return launch_fwd<T, 256, 1, 512>(x, probs, y, rows, inter, L, st);
+        }
         // a full 256-vector row (inter 2048): 192 lanes per row (the first
         // wavefront takes vectors 0-63 and 192-255, the others one vector per
-        // lane), three rows per 576-lane block, the block aligned before its
-        // loads: 85.1-85.5% of HBM peak (caches flushed before every launch),
-        // against 80.8-81.0% for the same shape unaligned, 79.8-80.6% for
-        // four 256-lane rows per 1024-lane block (aligned or not), 83.7-84.2%
-        // for two aligned 192-lane rows
-        if (nvec == 256) return launch_fwd<T, 192, 1, 576, true>(x, probs, y, rows, inter, L, st);
+        // lane), three rows per 576-lane block. bfloat16 with the block aligned
+        // before its loads: 85.1-85.5% of HBM peak (caches flushed before every
+        // launch), against 80.8-81.0% for the same shape unaligned, 79.8-80.6%
+        // for four 256-lane rows per 1024-lane block (aligned or not), 83.7-84.2%
+        // for two aligned 192-lane rows. float16 unaligned: 85.0%, against
+        // 82.9% aligned and 77.7% for four 256-lane rows.
+        if (nvec == 256) {
+            if constexpr (T == MOE_EPI_BF16) return launch_fwd<T, 192, 1, 576, true>(x, probs, y, rows, inter, L, st);
+            return launch_fwd<T, 192, 1, 576>(x, probs, y, rows, inter, L, st);
+        }
         // 193-255 vectors: 192 lanes per row, two rows per block (224 vectors: 82.4%
         // against 79.7% for 256 lanes, one row; 193 vectors: the same within 0.5%)
         if (nvec < 256) return launch_fwd<T, 192, 1, 384>(x, probs, y, rows, inter, L, st);
@@ -319,19 +334,30 @@ void dispatch_bwd(const void* x, const float* probs, const void* gy, void* gx, f
     if (nvec <= 128) return launch_bwd<T, 64, 2, 128>(x, probs, gy, gx, gp, rows, inter, L, st);
     if (nvec < 192) return launch_bwd<T, 128, 2, 256>(x, probs, gy, gx, gp, rows, inter, L, st);
     if constexpr (T == MOE_EPI_F32) {
+        // 256 vectors, aligned: 81.9% of HBM peak against 79.4% unaligned
+        if (nvec == 256) return launch_bwd<T, 384, 2, 384, true>(x, probs, gy, gx, gp, rows, inter, L, st);
         if (nvec <= 256) return launch_bwd<T, 384, 2, 384>(x, probs, gy, gx, gp, rows, inter, L, st);
         if (nvec <= 512) return launch_bwd<T, 640, 2, 640>(x, probs, gy, gx, gp, rows, inter, L, st);
         return launch_bwd<T, 512, 1, 1024>(x, probs, gy, gx, gp, rows, inter, L, st);
     } else {
-        // 192 vectors (inter 1536): one vector per lane of 192, three rows per
-        // block, aligned: 82.2% of HBM peak against 78.3% for two unaligned
-        // 256-lane rows per block
-        if (nvec == 192) return launch_bwd<T, 192, 1, 576, true>(x, probs, gy, gx, gp, rows, inter, L, st);
-        // 256 vectors (inter 2048): three 192-lane rows per block, aligned
-        // before the loads: 82.8-83.1% of HBM peak, against 78.6% unaligned,
-        // 81.1-82.0% with the first wavefront's two vectors loaded together,
-        // 79.6-80.5% for two 192-lane rows (aligned or not)
-        if (nvec == 256) return launch_bwd<T, 192, 1, 576, true>(x, probs, gy, gx, gp, rows, inter, L, st);
+        // 192 vectors (inter 1536), bfloat16: one vector per lane of 192, three
+        // rows per block, aligned: 82.2% of HBM peak against 78.3% for two
+        // unaligned 256-lane rows per block (the shape float16 keeps)
+        if (nvec == 192) {
+            if constexpr (T == MOE_EPI_BF16)
+                return launch_bwd<T, 192, 1, 576, true>(x, probs, gy, gx, gp, rows, inter, L, st);
+            return launch_bwd<T, 256, 1, 512>(x, probs, gy, gx, gp, rows, inter, L, st);
+        }
+        // 256 vectors (inter 2048): three 192-lane rows per block. bfloat16
+        // aligned before the loads: 82.8-83.1% of HBM peak, against 78.6%
+        // unaligned, 81.1-82.0% with the first wavefront's two vectors loaded
+        // together, 79.6-80.5% for two 192-lane rows (aligned or not). float16
+        // unaligned: 80.8%, against 76.5% aligned.
+        if (nvec == 256) {
+            if constexpr (T == MOE_EPI_BF16)
+                return launch_bwd<T, 192, 1, 576, true>(x, probs, gy, gx, gp, rows, inter, L, st);
+            return launch_bwd<T, 192, 1, 576>(x, probs, gy, gx, gp, rows, inter, L, st);
+        }
         if (nvec <= 256) return launch_bwd<T, 192, 1, 384>(x, probs, gy, gx, gp, rows, inter, L, st);
         if (nvec <= 512) return launch_bwd<T, 448, 1, 448>(x, probs, gy, gx, gp, rows, inter, L, st);
         return launch_bwd<T, 512, 2, 512>(x, probs, gy, gx, gp, rows, inter, L, st);
