@@ -196,6 +196,17 @@ __device__ __forceinline__ void wait_loads_but() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
+// A block barrier for LDS hazards only: this wavefront's LDS reads and writes
+// are complete, then the block meets. __syncthreads() would also wait for every
+// global store still in flight (its release fence), which in the epilogue put
+// the full store latency between one staged output tile and the next.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt left free (gfx9 encoding)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // ---- the pipelined main loop ------------------------------------------------
 //
 // Two LDS stages of BK = 64 (four 16-wide sub-steps). Per K step the
@@ -483,7 +494,13 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     const int32_t* __restrict__ offs, const float* __restrict__ probs, void* __restrict__ out,
     uint16_t* __restrict__ x_out, int64_t tokens, int64_t k_dim, int64_t n_dim, int64_t experts, float L,
     int64_t n_tiles, int64_t n_blocks) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[C::kLdsElems];
+    // One LDS object: the K-step stages (then the staging tile), followed by
+    // the tile rows' probabilities. (A second __shared__ array made the
+    // compiler attach alias scopes to LDS accesses, after which it no longer
+    // told the main loop's fragment reads from its direct-to-LDS loads and
+    // waited for every load in flight at each K step: twice the run time.)
+    __shared__ __attribute__((aligned(16))) uint16_t lds[C::kLdsElems + 2 * C::BM];
+    float* const ptile = reinterpret_cast<float*>(lds + C::kLdsElems);
     constexpr int MI = C::MI, NI = C::NI;
     constexpr bool kRouter = kEpi != Epi::kSwiglu;
 
@@ -518,8 +535,17 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
             acc_u[mi][ni] = f32x16{};
         }
 
+    // The tile rows' probabilities go straight into LDS (a direct load, one
+    // dword per lane; rows past the tile repeat its last row), in flight with
+    // the first K step's loads, which the main loop waits for before its first
+    // barrier. The epilogue then reads them from LDS.
+    if (wave < C::BM / 64) {
+        const int r = wave * 64 + lane;
+        __builtin_amdgcn_global_load_lds(probs + tr.row0 + (r < tr.rows ? r : tr.rows - 1),
+                                         (__attribute__((address_space(3))) void*)(ptile + wave * 64), 4, 0, 0);
+    }
     mainloop_pipe<C, kBuf>(lds, a_tile, g_tile, u_tile, tr.rows, ncols1, ncols2 > 0 ? ncols2 : 1, k_dim, acc_g, acc_u);
-    __syncthreads();  // all fragment reads done before the buffers become the staging tile
+    lds_barrier();  // all fragment reads done before the buffers become the staging tile
 
     uint16_t* stage = lds;
     if constexpr (kEpi == Epi::kSwiglu) {
@@ -529,7 +555,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int r = acc_row<C>(wm, mi, j, lane);
-                const float p = r < tr.rows ? probs[tr.row0 + r] : 0.0f;
+                const float p = ptile[r];
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni) {
                     const float g = round_bf16(acc_g[mi][ni][j]);
@@ -537,10 +563,10 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
                     stage[r * C::kLdo + acc_col<C>(wn, ni, lane)] = to_bf16(fwd_elem(g, u, p, L));
                 }
             }
-        __syncthreads();
+        lds_barrier();
         store_tile<C>(stage, y, n_dim, tr.row0, tr.rows, col1, n_dim);
         if constexpr (kWriteX) {
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -549,9 +575,9 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
                     for (int j = 0; j < 16; ++j)
                         stage[acc_row<C>(wm, mi, j, lane) * C::kLdo + acc_col<C>(wn, ni, lane)] =
                             to_bf16(acc_g[mi][ni][j]);
-            __syncthreads();
+            lds_barrier();
             store_tile<C>(stage, x_out, 2 * n_dim, tr.row0, tr.rows, col1, n_dim);
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -560,7 +586,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
                     for (int j = 0; j < 16; ++j)
                         stage[acc_row<C>(wm, mi, j, lane) * C::kLdo + acc_col<C>(wn, ni, lane)] =
                             to_bf16(acc_u[mi][ni][j]);
-            __syncthreads();
+            lds_barrier();
             store_tile<C>(stage, x_out + n_dim, 2 * n_dim, tr.row0, tr.rows, col1, n_dim);
         }
     } else if constexpr (kEpi == Epi::kRouterF32) {
@@ -578,20 +604,20 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
             const int ncols = half == 0 ? ncols1 : ncols2;
             const int64_t colb = half == 0 ? col1 : col2;
             if (ncols == 0) break;
-            if (half == 1) __syncthreads();  // the first half's stores have read the staging tile
+            if (half == 1) lds_barrier();  // the first half's stores have read the staging tile
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int r = acc_row<C>(wm, mi, j, lane);
-                    const float p = r < tr.rows ? probs[tr.row0 + r] : 0.0f;
+                    const float p = ptile[r];
 #pragma unroll
                     for (int ni = 0; ni < NI; ++ni) {
                         const float v = half == 0 ? acc_g[mi][ni][j] : acc_u[mi][ni][j];
                         stf[r * C::BN + sw(r, acc_col<C>(wn, ni, lane))] = round_bf16(v) * p;
                     }
                 }
-            __syncthreads();
+            lds_barrier();
             constexpr int kChunks = C::BM * C::BN / 4 / C::kThreads;
 #pragma unroll
             for (int i = 0; i < kChunks; ++i) {
@@ -606,20 +632,20 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
         uint16_t* o = static_cast<uint16_t*>(out);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            if (half == 1) __syncthreads();  // the first half's stores have read the staging tile
+            if (half == 1) lds_barrier();  // the first half's stores have read the staging tile
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int r = acc_row<C>(wm, mi, j, lane);
-                    const float p = r < tr.rows ? probs[tr.row0 + r] : 0.0f;
+                    const float p = ptile[r];
 #pragma unroll
                     for (int ni = 0; ni < NI; ++ni) {
                         const float v = half == 0 ? acc_g[mi][ni][j] : acc_u[mi][ni][j];
                         stage[r * C::kLdo + acc_col<C>(wn, ni, lane)] = to_bf16(round_bf16(v) * p);
                     }
                 }
-            __syncthreads();
+            lds_barrier();
             if (half == 0)
                 store_tile<C>(stage, o, n_dim, tr.row0, tr.rows, col1, col1 + ncols1);
             else if (ncols2 > 0)
