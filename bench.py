@@ -32,7 +32,13 @@ Prints one JSON line. Options:
                      served from them; the step time is then the sum of the
                      two kernels' event times
   --no-copy-ceiling  skip timing the 1 GiB device copy whose bandwidth the
-                     SwiGLU / router lines also report a fraction of
+                     SwiGLU / router lines also report a fraction of (it runs
+                     after the host-side input generation, before the
+                     settling and the warm-up steps)
+  --settle-seconds S SwiGLU / router: run the step untimed for S seconds
+                     (default 0.1) before the W warm-up steps, so that the
+                     timed steps see the GPU's steady state; the line reports
+                     how many steps that was (0 turns it off)
   --all              the four SwiGLU workloads and the router workload in
                      turn, one JSON line each (the default is the headline
                      workload alone, one line)
@@ -98,6 +104,8 @@ def parse_args():
                     help="SwiGLU / router: no cache flush between launches (default: a 1 GiB write before each)")
     ap.add_argument("--no-copy-ceiling", action="store_true",
                     help="SwiGLU / router: do not time the 1 GiB device copy (the box's copy ceiling)")
+    ap.add_argument("--settle-seconds", type=float, default=0.1,
+                    help="SwiGLU / router: run the step untimed for this long before the warm-up steps (0: off)")
     ap.add_argument("--all", action="store_true",
                     help="every SwiGLU and router workload in turn, one JSON line each")
     return ap.parse_args()
@@ -186,7 +194,10 @@ def load_traffic(kernel: str, workload) -> float | None:
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
-def copy_ceiling(steps: int = 20) -> dict:
+COPY_CEILING_LAUNCHES = 100
+
+
+def copy_ceiling(steps: int = COPY_CEILING_LAUNCHES) -> dict:
     """Bandwidth of a plain 1 GiB device-to-device copy on this machine (torch's
     copy_, carried out by the HIP runtime's copy kernel), bytes read plus bytes
     written over the average launch time: what a kernel that only moves data
@@ -206,8 +217,9 @@ def copy_ceiling(steps: int = 20) -> dict:
     torch.cuda.synchronize()
     avg = sum(a.elapsed_time(b) for a, b in evs) / steps
     gbs = 2 * n * 2 / (avg * 1e-3) / 1e9
+    # The two buffers go back to torch's cache, not to the driver, so that no
+    # release of device memory runs beside the launches timed next.
     del src, dst
-    torch.cuda.empty_cache()
     return {"GB/s": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS,
             "how": f"1 GiB device-to-device copy (torch copy_), read + written bytes over the average of {steps} "
                    "launches"}
@@ -261,18 +273,14 @@ def main():
         return down_main(args, DOWN_WORKLOADS[args.workload])
     if args.workload in COMBINE_WORKLOADS:
         return combine_main(args, COMBINE_WORKLOADS[args.workload])
-    ceiling = None
-    if not args.no_copy_ceiling:
-        print("[bench] timing a 1 GiB device copy (the copy ceiling)", file=sys.stderr, flush=True)
-        ceiling = copy_ceiling()
     if args.all:
         for name in WORKLOADS:  # the five SwiGLU / router workloads, one line each
-            epilogue_main(args, WORKLOADS[name], ceiling)
+            epilogue_main(args, WORKLOADS[name])
         return None
-    return epilogue_main(args, WORKLOADS[args.workload or HEADLINE], ceiling)
+    return epilogue_main(args, WORKLOADS[args.workload or HEADLINE])
 
 
-def epilogue_main(args, w, ceiling=None):
+def epilogue_main(args, w):
     """One clamped-SwiGLU or router-weight-multiply workload: forward + backward per step."""
     import numpy as np
     import torch
@@ -313,32 +321,61 @@ def epilogue_main(args, w, ceiling=None):
         bwd = lambda: epi.router_weight_mul_bwd(gy, x if want_gp else None, p, gx, gp)
     fwd_b, bwd_b = w.fwd_bytes(dt, od), w.bwd_bytes(want_gp, dt, od)
 
-    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        fwd()
-        bwd()
-    torch.cuda.synchronize()
-
-    E = lambda: torch.cuda.Event(enable_timing=True)
-    evs = [(E(), E(), E(), E()) for _ in range(args.steps)]
     # unless --warm: a 1 GiB write before each launch evicts L2 and the 256 MB
     # Infinity Cache, so that a workload smaller than them is not served from
     # them; the flushes lie outside the kernels' events
     scratch = None if args.warm else torch.empty((1 << 28,), dtype=torch.float32, device=dev)
+
+    # The copy ceiling is timed after the inputs are generated on the host and
+    # uploaded, so that the GPU is not idle between it and the steps below.
+    ceiling = None
+    if not args.no_copy_ceiling:
+        print("[bench] timing a 1 GiB device copy (the copy ceiling)", file=sys.stderr, flush=True)
+        ceiling = copy_ceiling(COPY_CEILING_LAUNCHES)
+
+    def step(ev=None):  # warm-up and timed steps are the same work
+        if scratch is not None:
+            scratch.zero_()
+        if ev:
+            ev[0].record()
+        fwd()
+        if ev:
+            ev[1].record()
+        if scratch is not None:
+            scratch.zero_()
+        if ev:
+            ev[2].record()
+        bwd()
+        if ev:
+            ev[3].record()
+
+    # Settling: the same step, untimed, for --settle-seconds before the W
+    # warm-up steps. When these kernels start on a GPU that has not run them
+    # for a while, launches 2 to ~15 ran up to 17% slower than the steady
+    # state and recovered step by step; 1000 back-to-back device copies
+    # (0.4 s) beforehand did not prevent it, while a run of the same steps
+    # about 10 s earlier did. The line reports the steps this took.
+    settle_steps, t = 0, time.perf_counter()
+    if args.settle_seconds > 0:
+        print(f"[bench] settling for {args.settle_seconds:g} s", file=sys.stderr, flush=True)
+    while time.perf_counter() - t < args.settle_seconds:
+        for _ in range(10):
+            step()
+        settle_steps += 10
+        torch.cuda.synchronize()
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [(E(), E(), E(), E()) for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1, e2, e3 in evs:
-        if scratch is not None:
-            scratch.zero_()
-        e0.record()
-        fwd()
-        e1.record()
-        if scratch is not None:
-            scratch.zero_()
-        e2.record()
-        bwd()
-        e3.record()
+    for ev in evs:
+        step(ev)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     fwd_ms = np.array([a.elapsed_time(b) for a, b, _, _ in evs])
@@ -419,6 +456,8 @@ def epilogue_main(args, w, ceiling=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"steps": settle_steps, "seconds": args.settle_seconds,
+                   "what": "untimed steps of the same work before the warm-up steps"},
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
