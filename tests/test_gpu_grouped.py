@@ -76,6 +76,27 @@ def check(d, tokens, hidden, inter, experts, L, what):
     say(f"{what}: x {sx}, y exact {sy['exact']:.5f}")
 
 
+def test_epilogue_reads_the_bf16_rounded_sums_not_the_accumulators():
+    """Designed inputs (tests/grouped_designed.py): exact binary32 sums that are not bf16 values,
+    and per row a probability that puts one column's output on different bf16 values under the
+    two readings of the epilogue's input. The kernel must give x = the bf16 roundings and, in
+    every target column, the oracle's y (the bf16-rounded reading) bit for bit."""
+    from tests import grouped_designed as gd
+    d = gd.build()
+    y, x = run(d, gd.TOKENS, gd.HIDDEN, gd.INTER, gd.EXPERTS, gd.LIMIT)
+    y_o, x_o = oracle.grouped_swiglu_fwd(d["a"], d["w_gate"], d["w_up"], d["offs"], d["probs"], gd.TOKENS,
+                                         gd.HIDDEN, gd.INTER, gd.EXPERTS, gd.LIMIT)
+    assert np.array_equal(x, x_o) and np.array_equal(x, d["x_bits"])
+    rows = np.arange(gd.TOKENS)
+    yt = y[rows, d["target"]]
+    assert np.array_equal(yt, y_o[rows, d["target"]]) and np.array_equal(yt, d["want_bits"])
+    assert (yt != d["other_bits"]).all()
+    st = assert_bf16_parity(y, y_o, "designed y")
+    y2, _ = run(d, gd.TOKENS, gd.HIDDEN, gd.INTER, gd.EXPERTS, gd.LIMIT, with_x=False)
+    assert np.array_equal(y2, y)
+    say(f"designed: {gd.TOKENS} target outputs on the bf16-rounded reading, y exact {st['exact']:.5f}")
+
+
 def test_small_named_workload():
     w = GROUPED_WORKLOADS["grouped_4096x1024x512_e5"]
     check(w.generate(), w.tokens, w.hidden, w.inter, w.experts, w.limit, w.name)

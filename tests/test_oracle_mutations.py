@@ -76,6 +76,10 @@ MUTANTS = [
     ("grouped: decreasing counts not clamped", "if (end < start) end = start;", ";"),
     ("grouped: sums rounded through binary32", "uint16_t g = oracle_f64_to_bf16(sum_scratch[t * 2 * inter + j]);",
      "uint16_t g = oracle_f32_to_bf16((float)sum_scratch[t * 2 * inter + j]);"),
+    ("grouped: epilogue on the binary32 sums, not their bf16 roundings",
+     "oracle_swiglu_point(oracle_bf16_to_f32(g), oracle_bf16_to_f32(u), probs[t], 0.0f, L, q);",
+     "oracle_swiglu_point((float)sum_scratch[t * 2 * inter + j], (float)sum_scratch[t * 2 * inter + inter + j], "
+     "probs[t], 0.0f, L, q);"),
     ("down: probability not applied", "oracle_store(out, t * hidden + n, out_dtype, out2 * probs[t]);",
      "oracle_store(out, t * hidden + n, out_dtype, out2);"),
     ("down: sum not rounded to bf16 first", "float out2 = oracle_bf16_to_f32(oracle_f64_to_bf16(s));",
@@ -131,6 +135,7 @@ def _pins():
         ("grouped per-expert scale", lambda o: gpins.test_per_expert_power_of_two_weights_select_the_expert(o)),
         ("grouped epilogue", lambda o: gpins.test_forward_is_the_epilogue_of_the_rounded_sums(o)),
         ("grouped tie", lambda o: gpins.test_sums_next_to_a_bf16_tie_are_rounded_once(o)),
+        ("grouped reading", lambda o: gpins.test_epilogue_reads_the_bf16_rounded_sums_not_the_accumulators(o)),
         ("down integer", lambda o: [npins.test_down_integer_products_and_power_of_two_probs(d, f, o)
                                     for d in (real_oracle.BF16, real_oracle.F32) for f in ([4, 4, 11], [11, 3, 20])]),
         ("down rational", lambda o: npins.test_down_exact_rational_sums_then_the_router_multiply(o)),

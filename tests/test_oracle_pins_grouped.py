@@ -205,3 +205,22 @@ def test_sums_next_to_a_bf16_tie_are_rounded_once(o):
         exact = sum(w)
         assert x[0, 0] == nearest_bf16(exact) == f64_to_bf16_exact(exact), (k, hex(x[0, 0]))
     assert nearest_bf16(1.0 + 2.0 ** -8 + 2.0 ** -30) == 0x3F81 and nearest_bf16(1.0 + 2.0 ** -8 - 2.0 ** -30) == 0x3F80
+
+
+def test_epilogue_reads_the_bf16_rounded_sums_not_the_accumulators(o):
+    """On the designed inputs of tests/grouped_designed.py, every grouped sum is exact in binary32
+    and not a bf16 value, and each row's probability puts, in one column, the clamped SwiGLU of
+    the bf16-rounded gate and up and that of the unrounded sums on different bf16 values (both
+    computed here in float64, away from any rounding midpoint). The oracle must give x = the
+    bf16 roundings of the sums and, in every target column, the first of the two."""
+    from tests import grouped_designed as gd
+    d = gd.build()
+    y, x = o.grouped_swiglu_fwd(d["a"], d["w_gate"], d["w_up"], d["offs"], d["probs"], gd.TOKENS, gd.HIDDEN,
+                                gd.INTER, gd.EXPERTS, gd.LIMIT)
+    assert np.array_equal(x, d["x_bits"])
+    yt = y[np.arange(gd.TOKENS), d["target"]]
+    assert np.array_equal(yt, d["want_bits"])
+    assert (yt != d["other_bits"]).all()
+    # the gate side and the up side are both exercised, with both signs of the result
+    assert (d["target"] < gd.INTER // 2).any() and (d["target"] >= gd.INTER // 2).any()
+    assert ((d["want_bits"] & 0x8000) != 0).any() and ((d["want_bits"] & 0x8000) == 0).any()
