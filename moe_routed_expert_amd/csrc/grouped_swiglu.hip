@@ -54,7 +54,7 @@
 //   * Tiles never straddle experts: each block finds its expert and row range
 //     from offs on the device (no host copy of offs), so a grid sized for
 //     the worst case, ceil(tokens / 256) + experts row tiles, covers any split.
-//   * Tile order: tiles are visited in groups of row tiles (4 for gate_up, 32
+//   * Tile order: tiles are visited in groups of row tiles (2 for gate_up, 32
 //     for the down projection), the row tile changing fastest, so that the
 //     blocks running together on one XCD share both their A tiles and their
 //     weight tiles in that XCD's L2. The hardware hands consecutive block ids
@@ -204,11 +204,14 @@ struct Cfg {
 };
 
 // The configurations the library launches (see the kernel-shape notes at the
-// top). They differ only in the tile group: 4 row tiles for the gate_up GEMM
+// top). They differ only in the tile group: 2 row tiles for the gate_up GEMM
 // (16 column tiles at inter 2048), 32 for the down projection (28 column
-// tiles at hidden 7168), each the best of a sweep (gate_up: 2-4 row tiles
-// 1107 TFLOP/s, 1 1094, 16 1079; down: 32 1023, 4 1011, 14 999, 7 968).
-using ProdGateUp = Cfg<256, 128, 4, 2, 2, 2, 4, 64>;
+// tiles at hidden 7168), each the best of a sweep. With the launched loop and
+// epilogue, A/B in one process: gate_up 2 row tiles 6.27-6.34 ms, 4 (the
+// earlier choice) 6.31-6.41, 1 6.40, 3 6.69, 8 6.49; down 32 3.29-3.30 ms,
+// 16 3.31-3.32, 24 3.33, 48 3.34, 64 3.35. (Earlier loops: gate_up 2-4 row
+// tiles 1107 TFLOP/s, 1 1094, 16 1079; down 32 1023, 4 1011, 14 999, 7 968.)
+using ProdGateUp = Cfg<256, 128, 4, 2, 2, 2, 2, 64>;
 using ProdDown = Cfg<256, 128, 4, 2, 2, 2, 32, 64>;
 
 // Swizzle of a row's chunks: any 8 consecutive rows, and any 16 consecutive
