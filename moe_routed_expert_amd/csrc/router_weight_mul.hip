@@ -226,16 +226,22 @@ void dispatch_fwd(const void* x, const float* probs, void* out, int64_t rows, in
     if (nvec < 128) return launch_fwd<TX, TO, 64, 2, 256>(x, probs, out, rows, hidden, st);
     if (nvec == 128) return launch_fwd<TX, TO, 128, 1, 256>(x, probs, out, rows, hidden, st);
     if (nvec < 192) return launch_fwd<TX, TO, 128, 2, 256>(x, probs, out, rows, hidden, st);
-    // 896 vectors (hidden 7168, the pages' model width) with bfloat16 x: shapes
+    // 896 vectors (hidden 7168, the pages' model width) with 16-bit x: shapes
     // from a second sweep, per dtype pair, with the option of aligned row loads
     // (align_block_loads, epi_common.h); caches flushed before every launch
-    if constexpr (TX == MOE_EPI_BF16) {
+    if constexpr (TX == MOE_EPI_BF16 || TX == MOE_EPI_F16) {
         if (nvec == 896) {
             // bf16 out: 320 lanes of two vectors a pass, three rows per block,
             // aligned: 79.7% of HBM peak against 76.3% for one unaligned row
-            // per block; fp32 out: 896 lanes, aligned: 83.2% against 74.8% for
-            // 512 lanes unaligned
-            if constexpr (TO == MOE_EPI_BF16) return launch_fwd<TX, TO, 320, 2, 960, true>(x, probs, out, rows, hidden, st);
+            // per block (two rows per block: the same); fp16 out: two rows per
+            // block, aligned: 80.7-81.8% against 77.4-77.6% for one unaligned
+            // row (three rows: 79.7-80.3%); fp32 out: 896 lanes, aligned: 83.2%
+            // (bf16 x) and 83.0% (fp16 x) against 74.8% and 73.7% for 512
+            // lanes unaligned
+            if constexpr (TX == MOE_EPI_BF16 && TO == MOE_EPI_BF16)
+                return launch_fwd<TX, TO, 320, 2, 960, true>(x, probs, out, rows, hidden, st);
+            if constexpr (TX == MOE_EPI_F16 && TO == MOE_EPI_F16)
+                return launch_fwd<TX, TO, 320, 2, 640, true>(x, probs, out, rows, hidden, st);
             if constexpr (TO == MOE_EPI_F32) return launch_fwd<TX, TO, 896, 1, 896, true>(x, probs, out, rows, hidden, st);
         }
     }
@@ -278,14 +284,23 @@ void dispatch_bwd(const void* go, const void* x, const float* probs, void* gx, f
     if (nvec <= 128) return launch_bwd<TX, TO, 64, 2, 128>(go, x, probs, gx, gp, rows, hidden, st);
     if (nvec < 192) return launch_bwd<TX, TO, 128, 2, 256>(go, x, probs, gx, gp, rows, hidden, st);
     // 896 vectors (hidden 7168): as for the forward, a second sweep per pair
-    if constexpr (TX == MOE_EPI_BF16) {
+    if constexpr (TX == MOE_EPI_BF16 || TX == MOE_EPI_F16) {
         if (nvec == 896) {
-            // bf16 grad_out, aligned: 81.3% of HBM peak against 77.7% unaligned;
-            // fp32 grad_out: 896 lanes, aligned: 83.8% against 81.1% unaligned
-            if constexpr (TO == MOE_EPI_BF16)
-                return launch_bwd<TX, TO, 448, 2, 896, true>(go, x, probs, gx, gp, rows, hidden, st);
+            // fp32 grad_out: 896 lanes, aligned: 83.8% of HBM peak against 81.1%
+            // unaligned (bf16 x), 83.8% against 80.9% (fp16 x)
             if constexpr (TO == MOE_EPI_F32)
                 return launch_bwd<TX, TO, 896, 1, 896, true>(go, x, probs, gx, gp, rows, hidden, st);
+            if constexpr (TO == TX) {
+                // without the probability gradient the backward only streams
+                // grad_out into grad_x, a 1:1 copy: the forward's 320 lanes of two
+                // vectors, two rows per block, aligned: 80.3% against 74.3% (bf16)
+                // and 73.9% (fp16) for the shape below
+                if (!gp) return launch_bwd<TX, TO, 320, 2, 640, true>(go, x, probs, gx, gp, rows, hidden, st);
+                // bf16 grad_out, aligned: 81.3% against 77.7% unaligned; fp16 keeps
+                // the unaligned 16-bit shape below (82.0-82.5%, aligned 81.8%)
+                if constexpr (TX == MOE_EPI_BF16)
+                    return launch_bwd<TX, TO, 448, 2, 896, true>(go, x, probs, gx, gp, rows, hidden, st);
+            }
         }
     }
     if constexpr (TX == MOE_EPI_F32) {
