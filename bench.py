@@ -217,7 +217,7 @@ def copy_ceiling(steps: int = COPY_CEILING_LAUNCHES) -> dict:
     torch.cuda.synchronize()
     avg = sum(a.elapsed_time(b) for a, b in evs) / steps
     gbs = 2 * n * 2 / (avg * 1e-3) / 1e9
-    # The two buffers go back to torch's cache, not to the driver, so that no
+    # The two buffers go back to torch's cache, not to the HIP runtime, so that no
     # release of device memory runs beside the launches timed next.
     del src, dst
     return {"GB/s": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS,
