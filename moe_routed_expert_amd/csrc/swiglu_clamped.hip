@@ -351,12 +351,18 @@ void dispatch_bwd(const void* x, const float* probs, const void* gy, void* gx, f
         // 256 vectors (inter 2048): three 192-lane rows per block. bfloat16
         // aligned before the loads: 82.8-83.1% of HBM peak, against 78.6%
         // unaligned, 81.1-82.0% with the first wavefront's two vectors loaded
-        // together, 79.6-80.5% for two 192-lane rows (aligned or not). float16
-        // unaligned: 80.8%, against 76.5% aligned.
+        // together, 79.6-80.5% for two 192-lane rows (aligned or not); without
+        // the probability gradient the same shape (81.1%; 81.4% for two
+        // 512-lane rows). float16, unaligned: two 192-lane rows per block,
+        // 82.3-82.7% against 81.0-81.3% for three; without the probability
+        // gradient two 512-lane rows (half the lanes idle, no row reduction):
+        // 82.2-82.5% against 77.4-77.7% for three 192-lane rows (with the
+        // reduction that shape falls to 70.4%).
         if (nvec == 256) {
             if constexpr (T == MOE_EPI_BF16)
                 return launch_bwd<T, 192, 1, 576, true>(x, probs, gy, gx, gp, rows, inter, L, st);
-            return launch_bwd<T, 192, 1, 576>(x, probs, gy, gx, gp, rows, inter, L, st);
+            if (!gp) return launch_bwd<T, 512, 1, 1024>(x, probs, gy, gx, gp, rows, inter, L, st);
+            return launch_bwd<T, 192, 1, 384>(x, probs, gy, gx, gp, rows, inter, L, st);
         }
         if (nvec <= 256) return launch_bwd<T, 192, 1, 384>(x, probs, gy, gx, gp, rows, inter, L, st);
         if (nvec <= 512) return launch_bwd<T, 448, 1, 448>(x, probs, gy, gx, gp, rows, inter, L, st);

@@ -73,10 +73,14 @@ def run_swiglu(d, rows, inter, L, dt, offset=0):
     y = dev(np.zeros((rows, inter), d["x"].dtype))
     gx = dev(np.zeros((rows, 2 * inter), d["x"].dtype))
     gp = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    gx2 = dev(np.zeros((rows, 2 * inter), d["x"].dtype))
     epi.swiglu_clamped_fwd(x, p, y, L)
     epi.swiglu_clamped_bwd(x, p, gy, gx, gp, L)
+    epi.swiglu_clamped_bwd(x, p, gy, gx2, None, L)   # without the probability gradient (its own launch shapes)
     torch.cuda.synchronize()
-    return to_host(y, dt), to_host(gx, dt), gp.cpu().numpy()
+    gx_h = to_host(gx, dt)
+    assert np.array_equal(to_host(gx2, dt).view(np.uint8), gx_h.view(np.uint8)), "grad_x differs without grad_probs"
+    return to_host(y, dt), gx_h, gp.cpu().numpy()
 
 
 @pytest.mark.parametrize("dt", ["f16", "f32"])
