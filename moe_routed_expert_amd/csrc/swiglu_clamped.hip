@@ -268,6 +268,15 @@ void launch_bwd(const void* x, const float* probs, const void* gy, void* gx, flo
                            gx, gp, rows, inter, L);
 }
 
+// Up to this many rows (64 per CU on the 256-CU part) a launch is short
+// enough that its ramp and tail weigh more than the steady stream: one row per
+// block, unaligned, spreads the last blocks better. bfloat16 at inter 2048,
+// caches flushed: 8192 rows, forward 61.2% of HBM peak against 58.6% for three
+// aligned 192-lane rows per block, backward 66.3% against 61.6%; 16384 rows,
+// 70.9 / 73.3% against 70.1 / 71.9%; 32768 rows even; 65536 rows and above
+// the three aligned rows lead by 3-4 points.
+constexpr int64_t kFewRows = 16384;
+
 template <int T>
 void dispatch_fwd(const void* x, const float* probs, void* y, int64_t rows, int64_t inter, float L, hipStream_t st) {
     const int64_t nvec = inter / 8;
@@ -309,7 +318,10 @@ void dispatch_fwd(const void* x, const float* probs, void* y, int64_t rows, int6
         // for two aligned 192-lane rows. float16 unaligned: 85.0%, against
         // 82.9% aligned and 77.7% for four 256-lane rows.
         if (nvec == 256) {
-            if constexpr (T == MOE_EPI_BF16) return launch_fwd<T, 192, 1, 576, true>(x, probs, y, rows, inter, L, st);
+            if constexpr (T == MOE_EPI_BF16) {
+                if (rows <= kFewRows) return launch_fwd<T, 128, 2, 256>(x, probs, y, rows, inter, L, st);
+                return launch_fwd<T, 192, 1, 576, true>(x, probs, y, rows, inter, L, st);
+            }
             return launch_fwd<T, 192, 1, 576>(x, probs, y, rows, inter, L, st);
         }
         // 193-255 vectors: 192 lanes per row, two rows per block (224 vectors: 82.4%
@@ -359,8 +371,10 @@ void dispatch_bwd(const void* x, const float* probs, const void* gy, void* gx, f
         // 82.2-82.5% against 77.4-77.7% for three 192-lane rows (with the
         // reduction that shape falls to 70.4%).
         if (nvec == 256) {
-            if constexpr (T == MOE_EPI_BF16)
+            if constexpr (T == MOE_EPI_BF16) {
+                if (rows <= kFewRows) return launch_bwd<T, 256, 1, 256>(x, probs, gy, gx, gp, rows, inter, L, st);
                 return launch_bwd<T, 192, 1, 576, true>(x, probs, gy, gx, gp, rows, inter, L, st);
+            }
             if (!gp) return launch_bwd<T, 512, 1, 1024>(x, probs, gy, gx, gp, rows, inter, L, st);
             return launch_bwd<T, 192, 1, 384>(x, probs, gy, gx, gp, rows, inter, L, st);
         }
