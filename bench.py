@@ -280,6 +280,104 @@ def main():
     return epilogue_main(args, WORKLOADS[args.workload or HEADLINE])
 
 
+# Bits of the storage types, for the parity check of the SwiGLU / router lines.
+_EXP_FRAC = {"bf16": (16, 0x7F80, 0x007F), "f16": (16, 0x7C00, 0x03FF), "f32": (32, 0x7F800000, 0x007FFFFF)}
+
+
+def _host_bits(t, dt: str):
+    import numpy as np
+    import torch
+    if dt == "f32":
+        return t.view(torch.int32).cpu().numpy().view(np.uint32)
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _as_bits(a, dt: str):
+    import numpy as np
+    return np.ascontiguousarray(a).view(np.uint32 if dt == "f32" else np.uint16)
+
+
+def compare_bits(got, want, dt: str, rows_per_chunk: int = 16384) -> dict:
+    """Element-by-element comparison of two arrays of one storage type (bit
+    patterns, rows first): the share of bit-identical elements, the largest
+    distance in units in the last place, and whether NaN positions, zero
+    positions and the signs of zeros all agree. Only the elements whose bits
+    differ are examined further."""
+    import numpy as np
+    nbits, exp, frac = _EXP_FRAC[dt]
+    mag_mask = (1 << (nbits - 1)) - 1
+    same = n = max_ulp = 0
+    specials_match = True
+    for r0 in range(0, got.shape[0], rows_per_chunk):
+        g = got[r0:r0 + rows_per_chunk].ravel()
+        w_ = want[r0:r0 + rows_per_chunk].ravel()
+        differ = g != w_
+        n += int(g.size)
+        same += int(g.size - np.count_nonzero(differ))
+        if not differ.any():
+            continue
+        gd, wd = g[differ].astype(np.int64), w_[differ].astype(np.int64)
+        nan_g = ((gd & exp) == exp) & ((gd & frac) != 0)
+        nan_w = ((wd & exp) == exp) & ((wd & frac) != 0)
+        both_nan = nan_g & nan_w            # NaN on both sides: the same position, payloads aside
+        if (nan_g ^ nan_w).any() or ((gd & mag_mask) == 0).any() or ((wd & mag_mask) == 0).any():
+            specials_match = False          # a NaN or a zero (or a zero's sign) on one side only
+        keep = ~(nan_g | nan_w)
+        og = np.where(gd >> (nbits - 1) == 1, -(gd & mag_mask), gd & mag_mask)[keep]
+        ow = np.where(wd >> (nbits - 1) == 1, -(wd & mag_mask), wd & mag_mask)[keep]
+        if og.size:
+            max_ulp = max(max_ulp, int(np.abs(og - ow).max()))
+        same += int(both_nan.sum())
+    return {"exact_frac": same / n if n else 1.0, "max_ulp": max_ulp, "zeros_and_nans_match": specials_match}
+
+
+def compare_dprobs(got, want, abs_sum) -> dict:
+    """The probability gradient against the oracle's: |difference| over the
+    row's sum of |terms| (the bar is 2e-5)."""
+    import numpy as np
+    err = np.abs(got.astype(np.float64) - want.astype(np.float64))
+    ratio = err / np.maximum(abs_sum, 1e-30)
+    return {"max_err_over_sum_abs_terms": float(ratio.max(initial=0.0))}
+
+
+def same_run_parity(oracle, w, d, dt: str, od: str, want_gp: bool, got_first, got_gx, got_gp, threads) -> dict:
+    """The SwiGLU or router outputs of one step (host bit patterns; got_gp
+    float32 or None) against one oracle pass over the same inputs d, element
+    by element, with the bar the GPU tests use."""
+    code = {"bf16": oracle.BF16, "f16": oracle.F16, "f32": oracle.F32}
+    rows, cols = w.rows, w.cols
+    if w.op == "swiglu":
+        want_first = oracle.swiglu_clamped_fwd_typed(d["x"], code[dt], d["probs"], rows, cols, w.limit,
+                                                     threads=threads)
+        ref_gx, ref_gp, ref_abs = oracle.swiglu_clamped_bwd_typed(d["x"], code[dt], d["probs"], d["grad_out"], rows,
+                                                                  cols, w.limit, want_grad_probs=want_gp,
+                                                                  threads=threads, with_abs_sum=True)
+    else:
+        want_first = oracle.router_weight_mul_fwd_typed(d["x"], code[dt], d["probs"], code[od], rows, cols,
+                                                        threads=threads)
+        ref_gx, ref_gp, ref_abs = oracle.router_weight_mul_bwd_typed(d["grad_out"], code[od], d["x"], code[dt],
+                                                                     d["probs"], rows, cols, want_grad_probs=want_gp,
+                                                                     threads=threads, with_abs_sum=True)
+    c_out = compare_bits(got_first, _as_bits(want_first, od).reshape(got_first.shape), od)
+    c_gx = compare_bits(got_gx, _as_bits(ref_gx, dt).reshape(got_gx.shape), dt)
+    c_gp = compare_dprobs(got_gp, ref_gp, ref_abs) if got_gp is not None and ref_abs is not None else None
+    if w.op == "router":   # one fp32 multiply, one rounding: bit-exact in every dtype
+        bar = "out and grad_x bit-exact; d_probs within 2e-5 of the sum of |terms|"
+        within = c_out["exact_frac"] == 1.0 and c_gx["exact_frac"] == 1.0
+    elif dt != "f32":
+        bar = ("y and grad_x within 1 ulp with zeros, their signs and NaNs bit-exact; "
+               "d_probs within 2e-5 of the sum of |terms|")
+        within = all(c["max_ulp"] <= 1 and c["zeros_and_nans_match"] for c in (c_out, c_gx))
+    else:
+        bar = ("fp32 storage: reported only. The bound is derived per element in the GPU tests: where sigma "
+               "underflows the outputs are tiny and their ulp counts large")
+        within = None
+    if within is not None and c_gp is not None:
+        within = within and c_gp["max_err_over_sum_abs_terms"] <= 2e-5
+    return {"rows": rows, "checked": "every element", "bar": bar, "within_bar": within,
+            ("y" if w.op == "swiglu" else "out"): c_out, "grad_x": c_gx, "grad_probs": c_gp}
+
+
 def epilogue_main(args, w):
     """One clamped-SwiGLU or router-weight-multiply workload: forward + backward per step."""
     import numpy as np
@@ -311,12 +409,14 @@ def epilogue_main(args, w):
         y = torch.empty((rows, cols), dtype=tdt[dt], device=dev)
         gx = torch.empty_like(x)
         names = ("swiglu_clamped_fwd", "swiglu_clamped_bwd")
+        first_out = y
         fwd = lambda: epi.swiglu_clamped_fwd(x, p, y, w.limit)
         bwd = lambda: epi.swiglu_clamped_bwd(x, p, gy, gx, gp, w.limit)
     else:
         out = torch.empty((rows, cols), dtype=tdt[od], device=dev)
         gx = torch.empty_like(x)
         names = ("router_weight_mul_fwd", "router_weight_mul_bwd")
+        first_out = out
         fwd = lambda: epi.router_weight_mul_fwd(x, p, out)
         bwd = lambda: epi.router_weight_mul_bwd(gy, x if want_gp else None, p, gx, gp)
     fwd_b, bwd_b = w.fwd_bytes(dt, od), w.bwd_bytes(want_gp, dt, od)
@@ -409,10 +509,17 @@ def epilogue_main(args, w):
                 "algorithmic_bytes_per_launch": kernels[dom]["algorithmic_bytes"]}
 
     cpu = cpu1 = None
+    parity = None
     if not args.no_cpu_baseline:
         import oracle
         threads = args.cpu_threads or oracle.default_threads()
         code = {"bf16": oracle.BF16, "f16": oracle.F16, "f32": oracle.F32}
+
+        # Parity on the same inputs in the same run: the outputs of the last
+        # timed step against one untimed oracle pass, element by element.
+        print(f"[bench] parity: the last timed step's outputs against one oracle pass", file=sys.stderr, flush=True)
+        parity = same_run_parity(oracle, w, d, dt, od, want_gp, _host_bits(first_out, od), _host_bits(gx, dt),
+                                 gp.cpu().numpy() if gp is not None else None, threads)
         print(f"[bench] oracle on the host ({threads} threads): whole-workload passes for >= {args.cpu_seconds:g} s",
               file=sys.stderr, flush=True)
 
@@ -476,6 +583,7 @@ def epilogue_main(args, w):
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     if cpu1 is not None:
         line["cpu_baseline_1thread"] = cpu1
