@@ -823,7 +823,7 @@ def combine_main(args, w):
     roofline = {"bound": "hbm", "kernel": name, "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": gbs / PEAK_HBM_GBS, "traffic": load_traffic(name, w), "algorithmic_bytes_per_launch": nbytes}
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
         import oracle
         threads = args.cpu_threads or oracle.default_threads()
@@ -831,6 +831,15 @@ def combine_main(args, w):
         code = {"bf16": oracle.BF16, "f16": oracle.F16, "f32": oracle.F32}[w.eo_dtype]
         eo_o = eo_np.view(np.float16) if w.eo_dtype == "f16" else eo_np
         sro = np.ascontiguousarray(row_of[:sample])
+        # parity in the same run: the last timed launch's output against one
+        # untimed oracle pass, every element, bit-exact (the same binary32
+        # additions in the same order)
+        print("[bench] parity: the last timed launch's output against one oracle pass", file=sys.stderr, flush=True)
+        want = oracle.moe_combine(eo_o, code, sro, rows, sample, w.top_k, w.hidden, threads=threads)
+        c = compare_bits(_host_bits(out, "f32"), _as_bits(want, "f32").reshape(w.tokens, w.hidden), "f32")
+        parity = {"rows": w.tokens, "checked": "every element", "bar": "bit-exact", "within_bar": c["exact_frac"] == 1.0,
+                  "out": c}
+        del want
         print(f"[bench] oracle on the host ({threads} threads): {sample} tokens per pass for >= "
               f"{args.cpu_seconds:g} s", file=sys.stderr, flush=True)
         passes, ct = oracle_timed(lambda: oracle.moe_combine(eo_o, code, sro, rows, sample, w.top_k, w.hidden,
@@ -861,6 +870,7 @@ def combine_main(args, w):
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     print(json.dumps(line), flush=True)
 
