@@ -638,7 +638,9 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
         // LDS) at a time, then stored as 16-byte row-contiguous chunks. Each
         // row's 16-byte chunks are XOR-swizzled by the row's low four bits, so
         // a wavefront's write (32 rows, one chunk each) spreads over the banks.
-        // Stores straight from the accumulators (4 bytes per lane) ran 13% slower.
+        // Stores straight from the accumulators ran slower: 13% with 4 bytes per
+        // lane, 9% with 16 (a lane's four consecutive columns, 32 bytes of a row
+        // per wavefront half and store).
         static_assert(C::BM * C::BN * 4 <= C::kLdsElems * 2, "an fp32 tile fits the LDS");
         static_assert(C::BN % 64 == 0, "the swizzle permutes chunks within 64-column groups");
         float* o = static_cast<float*>(out);
