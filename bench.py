@@ -299,8 +299,9 @@ def _as_bits(a, dt: str):
 
 def compare_bits(got, want, dt: str, rows_per_chunk: int = 16384) -> dict:
     """Element-by-element comparison of two arrays of one storage type (bit
-    patterns, rows first): the share of bit-identical elements, the largest
-    distance in units in the last place, and whether NaN positions, zero
+    patterns, rows first): the share of elements that are bit-identical (or
+    NaN on both sides, whatever the payloads), the largest distance in units
+    in the last place among the others, and whether NaN positions, zero
     positions and the signs of zeros all agree. Only the elements whose bits
     differ are examined further."""
     import numpy as np
