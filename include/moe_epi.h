@@ -12,7 +12,10 @@
  *             row-major with no padding: one probability per row
  *             ([rows] == [rows, 1]). The call only validates its arguments and
  *             queues the kernel on `stream`; results are ready when the stream
- *             reaches that point. Calls are thread-safe.
+ *             reaches that point. Calls are thread-safe. With no allocation,
+ *             memset or synchronisation inside, a call can be captured into a
+ *             HIP graph on `stream` and replayed; the graph then reads and
+ *             writes the buffers passed at capture.
  *   Dtypes    x, y, gradients of x/y: bfloat16. probs, grad_probs: float32.
  *             All arithmetic is float32; each bfloat16 result is rounded once,
  *             to nearest with ties to even.
