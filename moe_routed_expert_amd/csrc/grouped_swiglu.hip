@@ -103,22 +103,20 @@ namespace moe_epi {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Accumulator layout. v_mfma_f32_32x32x16 leaves C[8*(j/4) + 4*(l/32) + j%4][l%32]
-// in register j of lane l (checked on the GPU). The MFMAs take the weight
-// fragment as their first operand, so that 32-row side runs along the output
-// columns: lane l of tile (mi, ni) holds the outputs of block-tile row
-// acc_row(mi) and, in registers 4q .. 4q+3, of the four consecutive columns
-// from acc_col(ni, q).
+// Accumulator layout. v_mfma_f32_16x16x32_bf16 leaves C[4*(l/16) + j][l%16] in
+// register j of lane l. The MFMAs take the weight fragment as their first
+// operand, so that C's rows run along the output columns: lane l of tile
+// (mi, ni) holds the outputs of block-tile row acc_row(mi) and of the four
+// consecutive columns from acc_col(ni), one per register.
 template <class C>
 __device__ __forceinline__ int acc_row(int wm, int mi, int lane) {
-    return wm * (C::BM / C::WM) + mi * 32 + lane % 32;
+    return wm * (C::BM / C::WM) + mi * 16 + lane % 16;
 }
 template <class C>
-__device__ __forceinline__ int acc_col(int wn, int ni, int q, int lane) {
-    return wn * (C::BN / C::WN) + ni * 32 + 8 * q + 4 * (lane / 32);
+__device__ __forceinline__ int acc_col(int wn, int ni, int lane) {
+    return wn * (C::BN / C::WN) + ni * 16 + 4 * (lane / 16);
 }
 
 // Two fp32 values rounded to bf16 and packed, the first in the low half (one
@@ -134,27 +132,27 @@ __device__ __forceinline__ f32x2 round2_bf16(float a, float b) {
     return f32x2{__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u)};
 }
 
-// Eight consecutive bf16 outputs of one row, from registers 8h' .. 8h'+7 of a
-// tile (h' = half, 0 or 1), pair(j) giving the outputs of registers j and
-// j + 1 (j even). Before
-// the exchange a lane holds columns 16h' + 4h .. +3 and 16h' + 8 + 4h .. +3
-// (h = lane / 32); v_permlane32_swap trades the second group of lanes 0-31 for
-// the first group of lanes 32-63, after which lane l holds columns
-// 16h' + 8h .. 16h' + 8h + 7 in order, one 16-byte chunk.
+// Eight consecutive bf16 outputs of one row from two tiles of the same rows,
+// pair(t, j) giving the outputs of registers j and j + 1 (j = 0 or 2) of tile
+// t (0 or 1). Before the exchange lane l holds columns 4g .. 4g + 3 of both
+// tiles (g = l / 16, the lane's group of 16); v_permlane16_swap trades the
+// second tile's values of groups 0 and 2 for the first tile's values of
+// groups 1 and 3, after which a lane of group g holds columns
+// 8 (g / 2) .. 8 (g / 2) + 7 of tile g % 2 in order, one 16-byte chunk.
 template <class F>
-__device__ __forceinline__ u32x4 row_chunk(F&& pair, int half) {
-    const int j = 8 * half;
-    auto pk = [&](int k) {
-        const f32x2 v = pair(k);
+__device__ __forceinline__ u32x4 row_chunk(F&& pair) {
+    auto pk = [&](int t, int j) {
+        const f32x2 v = pair(t, j);
         return pk_bf16(v[0], v[1]);
     };
-    const uint32_t a0 = pk(j), a1 = pk(j + 2), b0 = pk(j + 4), b1 = pk(j + 6);
-    const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
-    const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+    const uint32_t x0 = pk(0, 0), x1 = pk(0, 2), y0 = pk(1, 0), y1 = pk(1, 2);
+    const auto s0 = __builtin_amdgcn_permlane16_swap(x0, y0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(x1, y1, false, false);
     return u32x4{s0[0], s1[0], s0[1], s1[1]};
 }
-// First column of that chunk within the tile's 32 columns.
-__device__ __forceinline__ int chunk_col(int half, int lane) { return 16 * half + 8 * (lane / 32); }
+// The tile (0 or 1) of the lane's chunk and its first column within that tile.
+__device__ __forceinline__ int chunk_tile(int lane) { return (lane / 16) % 2; }
+__device__ __forceinline__ int chunk_col(int lane) { return 8 * (lane / 32); }
 
 // Write the staged [BM][kLdo] tile's valid rows and columns to a row-major
 // bf16 matrix (ld elements per row) at (row0, col0) with 16-byte stores.
@@ -181,14 +179,14 @@ __device__ __forceinline__ void store_tile(const uint16_t* stage, uint16_t* __re
 // of LDS contiguously, so tiles are not padded: chunk kq of a row (BK / 8
 // chunks of 16 bytes) is placed at slot row * (BK / 8) + (kq ^ swz(row)),
 // which keeps the 16-byte fragment reads conflict-free.
-template <int BM_, int BN_, int WM_, int WN_, int S_, int OCC_, int GM_ = 1, int BK_ = 32>
+template <int BM_, int BN_, int WM_, int WN_, int S_, int OCC_, int GM_ = 1, int BK_ = 64>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, S = S_, OCC = OCC_, GM = GM_;
     static constexpr int kCpr = BK / 8;                // 16-byte chunks per row
-    static_assert(kCpr == 4 || kCpr == 8, "K steps of 32 or 64");
+    static_assert(kCpr == 8, "K steps of 64: two 32-wide MFMA sub-steps");
     static constexpr int kThreads = 64 * WM * WN;
-    static constexpr int MI = BM / (32 * WM);
-    static constexpr int NI = BN / (32 * WN);
+    static constexpr int MI = BM / (16 * WM);           // 16 x 16 MFMA tiles per wavefront
+    static constexpr int NI = BN / (16 * WN);
     static constexpr int kAElems = BM * BK;            // no padding
     static constexpr int kWElems = BN * BK;
     static constexpr int kStageElems = kAElems + 2 * kWElems;
@@ -196,7 +194,8 @@ struct Cfg {
     static constexpr int kAChunks = BM * BK / 8 / kThreads;
     static constexpr int kWChunks = BN * BK / 8 / kThreads;
     static constexpr int kLdsElems = S * kStageElems > BM * kLdo ? S * kStageElems : BM * kLdo;
-    static_assert(MI >= 1 && NI >= 1 && BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "whole MFMA tiles");
+    static_assert(MI >= 1 && NI >= 2 && NI % 2 == 0 && BM % (16 * WM) == 0 && BN % (16 * WN) == 0,
+                  "whole MFMA tiles, pairs of column tiles for the epilogue's exchange");
     static_assert(kAChunks >= 1 && kWChunks >= 1 && BM * BK % (8 * kThreads) == 0 && BN * BK % (8 * kThreads) == 0,
                   "whole 16-byte chunks per thread");
     static_assert(S == 2, "two LDS stages");
@@ -214,14 +213,17 @@ struct Cfg {
 using ProdGateUp = Cfg<256, 128, 4, 2, 2, 2, 2, 64>;
 using ProdDown = Cfg<256, 128, 4, 2, 2, 2, 32, 64>;
 
-// Swizzle of a row's chunks: any 8 consecutive rows, and any 16 consecutive
-// rows taken 4 or 8 apart, put the same chunk in different 16-byte bank groups.
+// Swizzle of a row's eight chunks. A fragment read takes one chunk of 16
+// consecutive rows starting at a multiple of 16; with rows of 128 bytes, row t
+// of those puts it in 16-byte bank group (t % 2) * 8 + (kq ^ swz), and over the
+// 16 rows these are the 16 different groups of the 64 banks (any 8 of the rows
+// from a multiple of 8: 8 different groups of 32 banks). It depends on the row
+// modulo 16 only, so the fragments of tiles 16 rows apart sit at a constant
+// distance and share their address register.
 template <int kCpr>
 __device__ __forceinline__ int swz(int row) {
-    if constexpr (kCpr == 4)
-        return ((row >> 1) ^ (row >> 3)) & 3;
-    else
-        return (row ^ (row >> 3)) & 7;
+    static_assert(kCpr == 8, "rows of eight chunks");
+    return (row & 7) ^ ((row >> 3) & 1);
 }
 
 // Slot (in 16-byte units) of chunk kq of row `row` in a swizzled tile.
@@ -254,15 +256,15 @@ __device__ __forceinline__ void lds_barrier() {
 
 // ---- the pipelined main loop ------------------------------------------------
 //
-// Two LDS stages of BK = 64 (four 16-wide sub-steps). Per K step the
-// wavefront runs sub-steps 0-2 with the next sub-step's fragments read while
-// the current sub-step's MFMAs run; then it waits for its own loads of the
-// next stage and for its last fragment reads of this stage, and the block
-// meets at one barrier. After it, nobody reads this stage any more and the
-// next stage is complete, so the loads of the stage after next go into this
-// stage's buffer and the next stage's first fragments are read, both while
-// sub-step 3's MFMAs run. Only the next stage's loads are in flight at the
-// barrier, so the wait is simply for all of them.
+// Two LDS stages of BK = 64, each two 32-wide sub-steps of
+// v_mfma_f32_16x16x32_bf16. Per K step the wavefront runs sub-step 0 with
+// sub-step 1's fragments read while its MFMAs run; then it waits for its own
+// loads of the next stage and for its fragment reads of this stage, and the
+// block meets at one barrier. After it, nobody reads this stage any more and
+// the next stage is complete, so the loads of the stage after next go into
+// this stage's buffer and the next stage's first fragments are read, both
+// while sub-step 1's MFMAs run. Only the next stage's loads are in flight at
+// the barrier, so the wait is simply for all of them.
 //
 // Loads are issued without row bounds branches: a lane whose row lies past the
 // tile's valid rows loads the last valid row instead (its results are never
@@ -353,6 +355,42 @@ struct PipeLoads {
     __device__ __forceinline__ static void zero(uint16_t* dst) {
         *reinterpret_cast<u32x4*>(dst) = u32x4{0u, 0u, 0u, 0u};
     }
+    // Load number i (numbered as in issue_one) of the K step kt that crosses
+    // the end of K, in pointer form from the buffer offsets: chunks past k_dim
+    // are written as zeros.
+    __device__ __forceinline__ void issue_one_tail(const Buf& b, const uint16_t* a_tile, const uint16_t* g_tile,
+                                                   const uint16_t* u_tile, uint16_t* st, int64_t kt, int i,
+                                                   int64_t k_dim) const {
+        // the thread index through an empty asm, so that nothing derived from
+        // it is hoisted out of the main loop to sit in registers for this path
+        int tid = static_cast<int>(threadIdx.x);
+        asm volatile("" : "+v"(tid));
+        const int lane = tid % 64, wave = tid / 64;
+        const uint16_t* tile;
+        uint32_t voff;
+        uint16_t* dst;
+        int slot0;
+        if (i < kA) {
+            slot0 = i * C::kThreads + wave * 64;
+            tile = a_tile;
+            voff = b.va[i];
+            dst = st + slot0 * 8;
+        } else {
+            const int j = (i - kA) / 2;
+            slot0 = j * C::kThreads + wave * 64;
+            const bool up = (i - kA) % 2 == 1;
+            tile = up ? u_tile : g_tile;
+            voff = up ? b.vu[j] : b.vg[j];
+            dst = st + C::kAElems + (up ? C::kWElems : 0) + slot0 * 8;
+        }
+        const int row = (slot0 + lane) / C::kCpr;
+        const int kq = ((slot0 + lane) % C::kCpr) ^ swz<C::kCpr>(row);
+        const int64_t k0 = kt * C::BK;
+        if (k0 + kq * 8 < k_dim)
+            load(tile + voff / 2 + k0, dst);
+        else
+            zero(dst + lane * 8);
+    }
 
     // Loads of K step kt into `st` (one stage of LDS).
     __device__ __forceinline__ void issue(uint16_t* st, int64_t kt, int64_t k_dim) const {
@@ -391,137 +429,148 @@ struct PipeLoads {
     }
 };
 
-template <class C, bool kBuf>
+// The main loop's three forms, chosen by the host from k_dim.
+enum Loop : int {
+    kPtrLoop = 0,   // pointer-form loads (k_dim above kBufMaxK)
+    kBufLoop = 1,   // buffer-form loads, k_dim a multiple of BK
+    kBufTail = 2,   // buffer-form loads, and a last K step that crosses the end of K
+};
+
+template <class C, int kLoop>
 __device__ __forceinline__ void mainloop_pipe(uint16_t* lds, const uint16_t* a_tile, const uint16_t* g_tile,
                                               const uint16_t* u_tile, int arows, int grows, int urows,
-                                              int64_t k_dim, f32x16 (&acc_g)[C::MI][C::NI],
-                                              f32x16 (&acc_u)[C::MI][C::NI]) {
-    constexpr int MI = C::MI, NI = C::NI, KK = C::BK / 16;
-    static_assert(C::S == 2 && KK >= 2, "two stages of at least two sub-steps");
+                                              int64_t k_dim, f32x4 (&acc_g)[C::MI][C::NI],
+                                              f32x4 (&acc_u)[C::MI][C::NI]) {
+    constexpr int MI = C::MI, NI = C::NI, kMf = 2 * MI * NI;
+    static_assert(C::S == 2 && C::BK == 64, "two stages of two 32-wide sub-steps");
     const int lane = static_cast<int>(threadIdx.x) % 64;
     const int wave = static_cast<int>(threadIdx.x) / 64;
     const int wm = wave / C::WN, wn = wave % C::WN;
     const PipeLoads<C> ld(a_tile, g_tile, u_tile, arows, grows, urows, k_dim);
     const int64_t nk = (k_dim + C::BK - 1) / C::BK;
 
-    bf16x8 fa[2][MI], fg[2][NI], fu[2][NI];
-    auto read = [&](const uint16_t* stage, int b, int kk) {
-        const uint16_t* sa = stage;
-        const uint16_t* sg = stage + C::kAElems;
-        const uint16_t* su = stage + C::kAElems + C::kWElems;
-        const int kq = kk * 2 + lane / 32;
+    // Fragments (16 rows x 32 k, eight bf16 per lane: row lane % 16, one of
+    // the sub-step's four 16-byte chunks of that row per group of 16 lanes),
+    // one sub-step's worth: each is replaced by the next sub-step's once the
+    // MFMAs that use it have issued, which keeps the loop within 256 registers
+    // beside the 128 accumulators. Which lanes read which chunk is free as long
+    // as A and the weights agree; lanes l and l + 32 read adjacent chunks (as
+    // the two halves of a 32 x 32 fragment did): with lanes l and l + 16 on
+    // adjacent chunks instead, the same reads kept the LDS busy 46% of the
+    // time against 24%, and the kernels ran 0.7-1.3% slower.
+    bf16x8 fa[MI], fg[NI], fu[NI];
+    const int kq0 = ((lane / 16) & 1) * 2 + lane / 32;
+    auto read_a = [&](const uint16_t* stage, int kk, int mi) {
+        fa[mi] = frag_swz<C::kCpr>(stage, wm * (C::BM / C::WM) + mi * 16 + lane % 16, 4 * kk + kq0);
+    };
+    auto read_w = [&](const uint16_t* stage, int kk, int ni) {
+        const int row = wn * (C::BN / C::WN) + ni * 16 + lane % 16;
+        fg[ni] = frag_swz<C::kCpr>(stage + C::kAElems, row, 4 * kk + kq0);
+        fu[ni] = frag_swz<C::kCpr>(stage + C::kAElems + C::kWElems, row, 4 * kk + kq0);
+    };
+    // MFMA i of a sub-step: the column tile outermost, then the row tile, gate
+    // before up; weight fragment first (see acc_row / acc_col).
+    auto mfma = [&](int i) {
+        const int ni = i / (2 * MI), mi = (i / 2) % MI;
+        if (i % 2 == 0)
+            acc_g[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fg[ni], fa[mi], acc_g[mi][ni], 0, 0, 0);
+        else
+            acc_u[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fu[ni], fa[mi], acc_u[mi][ni], 0, 0, 0);
+    };
+    // The next sub-step's reads (sub-step kk of `stage`) that follow MFMA i:
+    // a column tile's weight fragments after the last MFMA using them, and in
+    // the last column tile, each A fragment after its last MFMA.
+    auto reads_after = [&](int i, const uint16_t* stage, int kk) {
+        if (i >= 2 * MI * (NI - 1) && i % 2 == 1) read_a(stage, kk, (i / 2) % MI);
+        if (i % (2 * MI) == 2 * MI - 1) read_w(stage, kk, i / (2 * MI));
+    };
+    // A sub-step with the next one's reads, pinned in this order (left to
+    // itself, the compiler issued the reads after the MFMAs and waited for
+    // them at the start of every sub-step).
+    auto substep = [&](const uint16_t* next_stage, int next_kk) {
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-            fa[b][mi] = frag_swz<C::kCpr>(sa, wm * (C::BM / C::WM) + mi * 32 + lane % 32, kq);
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-            fg[b][ni] = frag_swz<C::kCpr>(sg, wn * (C::BN / C::WN) + ni * 32 + lane % 32, kq);
-            fu[b][ni] = frag_swz<C::kCpr>(su, wn * (C::BN / C::WN) + ni * 32 + lane % 32, kq);
+        for (int i = 0; i < kMf; ++i) {
+            mfma(i);
+            reads_after(i, next_stage, next_kk);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // weight fragment first: see acc_row / acc_col
-    auto mfma = [&](int b) {
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni) {
-                acc_g[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fg[b][ni], fa[b][mi], acc_g[mi][ni], 0, 0, 0);
-                acc_u[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fu[b][ni], fa[b][mi], acc_u[mi][ni], 0, 0, 0);
-            }
-    };
-    // one fragment read of the next sub-step after each of this sub-step's
-    // first MFMAs (left to itself, the compiler issued the reads after the
-    // MFMAs and waited for them at the start of every sub-step)
-    auto interleave = [&]() {
-        constexpr int kReads = MI + 2 * NI, kMfmas = 2 * MI * NI;
-#pragma unroll
-        for (int i = 0; i < kReads; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - kReads, 0);
+    auto block_barrier = [&]() {  // own loads landed, own reads done, then the block meets
+        wait_loads_but<0>();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     ld.issue(lds, 0, k_dim);
-    wait_loads_but<0>();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    block_barrier();
     if (nk > 1) ld.issue(lds + C::kStageElems, 1, k_dim);
-    read(lds, 0, 0);
+    // the first sub-step's fragments, read in the loop's order, so that the
+    // waits at the top of the loop can count the reads still in flight
+#pragma unroll
+    for (int i = 0; i < kMf; ++i) reads_after(i, lds, 0);
 
-    int64_t kt = 0;
-    if constexpr (kBuf) {
-        // While the step after next is a full K step, the last sub-step issues
-        // its loads in buffer form one after each MFMA, with the next step's
-        // first fragment reads in between, in a branch-free loop body. Issued
-        // together before the MFMAs, the loads held the wavefronts at issue
-        // while the MFMA units idled (1072 against 1174 TFLOP/s for gate_up).
-        constexpr int kLoads = C::kAChunks + 2 * C::kWChunks, kReads = MI + 2 * NI, kMf = 2 * MI * NI;
-        static_assert(kLoads <= kMf && kReads <= kMf, "one load and one read per MFMA at most");
+    if constexpr (kLoop != kPtrLoop) {
+        // The loop runs from the middle of one K step to the middle of the
+        // next, so that its head follows a barrier (where every read has been
+        // waited for) and the waits between sub-steps are counted exactly.
+        // Sub-step 1 of step kt issues the loads of step kt + 2, one after
+        // every kEvery-th MFMA, between the reads of step kt + 1's first
+        // fragments: in buffer form while that step is a full K step, in
+        // pointer form with zeros past K for the step that crosses the end of
+        // K (uniform branches). Issued together before the MFMAs, the loads held
+        // the wavefronts at issue while the MFMA units idled (1072 against 1174
+        // TFLOP/s for gate_up). The step that crosses the end of K has a form of
+        // its own (kBufTail): its zero fill writes LDS, after which the compiler
+        // can no longer count the fragment reads in flight and waits for all of
+        // them at the start of every sub-step.
+        constexpr int kLoads = C::kAChunks + 2 * C::kWChunks, kEvery = kMf / kLoads;
+        static_assert(kEvery >= 1, "one load per MFMA at most");
         const typename PipeLoads<C>::Buf bufs = ld.buffers(a_tile, g_tile, u_tile);
-        const int64_t nmain = nk - (k_dim % C::BK == 0 ? 2 : 3);
-        constexpr int b = (KK - 1) & 1;
-        for (; kt < nmain; ++kt) {
+        // k_dim <= kBufMaxK here, so step counts fit 32 bits (scalar compares)
+        const int nk32 = static_cast<int>(nk), nfull = static_cast<int>(k_dim / C::BK);
+        substep(lds, 1);  // step 0, sub-step 0
+        block_barrier();
+        for (int kt = 0; kt + 1 < nk32; ++kt) {
             uint16_t* cur = lds + (kt & 1) * C::kStageElems;
             const uint16_t* nxt = lds + ((kt + 1) & 1) * C::kStageElems;
-#pragma unroll
-            for (int kk = 0; kk + 1 < KK; ++kk) {
-                read(cur, (kk + 1) & 1, kk + 1);
-                mfma(kk & 1);
-                interleave();
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            wait_loads_but<0>();
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
-            const int kq = lane / 32;
+            const int kn = kt + 2;
 #pragma unroll
             for (int i = 0; i < kMf; ++i) {
-                const int mi = i / (2 * NI), ni = (i / 2) % NI;
-                if (i % 2 == 0)
-                    acc_g[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fg[b][ni], fa[b][mi], acc_g[mi][ni], 0, 0, 0);
-                else
-                    acc_u[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fu[b][ni], fa[b][mi], acc_u[mi][ni], 0, 0, 0);
-                if (i < kLoads) ld.issue_one(bufs, cur, kt + 2, i);
-                if (i < MI) {
-                    fa[0][i] = frag_swz<C::kCpr>(nxt, wm * (C::BM / C::WM) + i * 32 + lane % 32, kq);
-                } else if (i < kReads) {
-                    const int j = (i - MI) / 2;
-                    const uint16_t* w = nxt + C::kAElems + ((i - MI) % 2) * C::kWElems;
-                    const bf16x8 f = frag_swz<C::kCpr>(w, wn * (C::BN / C::WN) + j * 32 + lane % 32, kq);
-                    if ((i - MI) % 2 == 0)
-                        fg[0][j] = f;
-                    else
-                        fu[0][j] = f;
+                mfma(i);
+                if (i % kEvery == 0 && i / kEvery < kLoads) {
+                    if (kn < nfull) {
+                        ld.issue_one(bufs, cur, kn, i / kEvery);
+                    } else if constexpr (kLoop == kBufTail) {
+                        if (kn < nk32)
+                            ld.issue_one_tail(bufs, a_tile, g_tile, u_tile, cur, kn, i / kEvery, k_dim);
+                    }
                 }
-                __builtin_amdgcn_sched_barrier(0);  // keep this order: MFMA, load, read
+                reads_after(i, nxt, 0);
+                __builtin_amdgcn_sched_barrier(0);  // keep this order: MFMA, load, reads
+            }
+            substep(nxt, 1);  // step kt + 1, sub-step 0
+            block_barrier();
+        }
+#pragma unroll
+        for (int i = 0; i < kMf; ++i) mfma(i);  // the last step's sub-step 1
+        __builtin_amdgcn_sched_barrier(0);
+    } else {
+        for (int64_t kt = 0; kt < nk; ++kt) {
+            uint16_t* cur = lds + (kt & 1) * C::kStageElems;
+            const uint16_t* nxt = lds + ((kt + 1) & 1) * C::kStageElems;
+            substep(cur, 1);
+            if (kt + 1 < nk) {
+                block_barrier();
+                if (kt + 2 < nk) ld.issue(cur, kt + 2, k_dim);
+                substep(nxt, 0);
+            } else {
+#pragma unroll
+                for (int i = 0; i < kMf; ++i) mfma(i);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-    }
-    for (; kt < nk; ++kt) {
-        uint16_t* cur = lds + (kt & 1) * C::kStageElems;
-        uint16_t* nxt = lds + ((kt + 1) & 1) * C::kStageElems;
-#pragma unroll
-        for (int kk = 0; kk + 1 < KK; ++kk) {
-            read(cur, (kk + 1) & 1, kk + 1);
-            mfma(kk & 1);
-            interleave();
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (kt + 1 < nk) {
-            // own loads of the next stage landed, own reads of this stage done; then the block meets
-            wait_loads_but<0>();
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            if (kt + 2 < nk) ld.issue(cur, kt + 2, k_dim);
-            read(nxt, 0, 0);
-        }
-        mfma((KK - 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -534,7 +583,7 @@ enum class Epi { kSwiglu, kRouterBf16, kRouterF32 };
 // A grouped GEMM over rows grouped by expert: the reduction runs over k_dim
 // (hidden for gate_up, inter for the down projection); n_dim is the width of
 // each weight tensor's output (inter for gate_up, hidden for down).
-template <class C, Epi kEpi, bool kWriteX, bool kBuf>
+template <class C, Epi kEpi, bool kWriteX, int kLoop>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::OCC))) void grouped_gemm_kernel(
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w2,
     const int32_t* __restrict__ offs, const float* __restrict__ probs, void* __restrict__ out,
@@ -572,13 +621,13 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     const int wave = static_cast<int>(threadIdx.x) / 64;
     const int wm = wave / C::WN, wn = wave % C::WN;
 
-    f32x16 acc_g[MI][NI], acc_u[MI][NI];
+    f32x4 acc_g[MI][NI], acc_u[MI][NI];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
-            acc_g[mi][ni] = f32x16{};
-            acc_u[mi][ni] = f32x16{};
+            acc_g[mi][ni] = f32x4{};
+            acc_u[mi][ni] = f32x4{};
         }
 
     // The tile rows' probabilities go straight into LDS (a direct load, one
@@ -590,7 +639,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
         __builtin_amdgcn_global_load_lds(probs + tr.row0 + (r < tr.rows ? r : tr.rows - 1),
                                          (__attribute__((address_space(3))) void*)(ptile + wave * 64), 4, 0, 0);
     }
-    mainloop_pipe<C, kBuf>(lds, a_tile, g_tile, u_tile, tr.rows, ncols1, ncols2 > 0 ? ncols2 : 1, k_dim, acc_g, acc_u);
+    mainloop_pipe<C, kLoop>(lds, a_tile, g_tile, u_tile, tr.rows, ncols1, ncols2 > 0 ? ncols2 : 1, k_dim, acc_g, acc_u);
     lds_barrier();  // all fragment reads done before the buffers become the staging tile
 
     // Each staged output tile is written to LDS in 16-byte row chunks (eight
@@ -600,20 +649,19 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     if constexpr (kEpi == Epi::kSwiglu) {
         uint16_t* y = static_cast<uint16_t*>(out);
         // stage one bf16 tile: pair(mi, ni, j, p) gives the outputs of registers
-        // j and j + 1 of tile (mi, ni), p the probability of its row
+        // j and j + 1 of tile (mi, ni), p the probability of its row; column
+        // tiles ni and ni + 1 are exchanged together (row_chunk)
         auto stage_bf16 = [&](auto&& pair) {
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
                 const int r = acc_row<C>(wm, mi, lane);
                 const float p = ptile[r];
 #pragma unroll
-                for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const u32x4 v = row_chunk([&](int j) { return pair(mi, ni, j, p); }, h);
-                        *reinterpret_cast<u32x4*>(stage + r * C::kLdo + acc_col<C>(wn, ni, 0, 0) +
-                                                  chunk_col(h, lane)) = v;
-                    }
+                for (int ni = 0; ni < NI; ni += 2) {
+                    const u32x4 v = row_chunk([&](int t, int j) { return pair(mi, ni + t, j, p); });
+                    *reinterpret_cast<u32x4*>(stage + r * C::kLdo + acc_col<C>(wn, ni + chunk_tile(lane), 0) +
+                                              chunk_col(lane)) = v;
+                }
             }
         };
         stage_bf16([&](int mi, int ni, int j, float p) {
@@ -657,14 +705,12 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
                 const int r = acc_row<C>(wm, mi, lane);
                 const float p = ptile[r];
 #pragma unroll
-                for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x16& v = half == 0 ? acc_g[mi][ni] : acc_u[mi][ni];
-                        const f32x2 lo = round2_bf16(v[4 * q], v[4 * q + 1]), hi = round2_bf16(v[4 * q + 2], v[4 * q + 3]);
-                        const f32x4 w{lo[0] * p, lo[1] * p, hi[0] * p, hi[1] * p};
-                        *reinterpret_cast<f32x4*>(stf + r * C::BN + sw(r, acc_col<C>(wn, ni, q, lane))) = w;
-                    }
+                for (int ni = 0; ni < NI; ++ni) {
+                    const f32x4& v = half == 0 ? acc_g[mi][ni] : acc_u[mi][ni];
+                    const f32x2 lo = round2_bf16(v[0], v[1]), hi = round2_bf16(v[2], v[3]);
+                    const f32x4 w{lo[0] * p, lo[1] * p, hi[0] * p, hi[1] * p};
+                    *reinterpret_cast<f32x4*>(stf + r * C::BN + sw(r, acc_col<C>(wn, ni, lane))) = w;
+                }
             }
             lds_barrier();
             constexpr int kChunks = C::BM * C::BN / 4 / C::kThreads;
@@ -687,17 +733,15 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
                 const int r = acc_row<C>(wm, mi, lane);
                 const float p = ptile[r];
 #pragma unroll
-                for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const f32x16& v = half == 0 ? acc_g[mi][ni] : acc_u[mi][ni];
-                        const u32x4 c = row_chunk([&](int j) {
-                            const f32x2 r2 = round2_bf16(v[j], v[j + 1]);
-                            return f32x2{r2[0] * p, r2[1] * p};
-                        }, h);
-                        *reinterpret_cast<u32x4*>(stage + r * C::kLdo + acc_col<C>(wn, ni, 0, 0) +
-                                                  chunk_col(h, lane)) = c;
-                    }
+                for (int ni = 0; ni < NI; ni += 2) {
+                    const u32x4 c = row_chunk([&](int t, int j) {
+                        const f32x4& v = half == 0 ? acc_g[mi][ni + t] : acc_u[mi][ni + t];
+                        const f32x2 r2 = round2_bf16(v[j], v[j + 1]);
+                        return f32x2{r2[0] * p, r2[1] * p};
+                    });
+                    *reinterpret_cast<u32x4*>(stage + r * C::kLdo + acc_col<C>(wn, ni + chunk_tile(lane), 0) +
+                                              chunk_col(lane)) = c;
+                }
             }
             lds_barrier();
             if (half == 0)
@@ -715,17 +759,19 @@ template <class C>
 constexpr int64_t kBufMaxK = ((int64_t{1} << 31) - 1) / (2 * (C::BM + 1));
 
 template <class C, Epi kEpi, bool kWriteX>
-void launch_kernel(bool buf, int64_t grid, hipStream_t st, const uint16_t* a, const uint16_t* w1, const uint16_t* w2,
+void launch_kernel(int loop, int64_t grid, hipStream_t st, const uint16_t* a, const uint16_t* w1, const uint16_t* w2,
                    const int32_t* offs, const float* probs, void* out, uint16_t* x_out, int64_t tokens, int64_t k_dim,
                    int64_t n_dim, int64_t experts, float limit, int64_t n_tiles, int64_t n_blocks) {
-    if (buf)
-        hipLaunchKernelGGL((grouped_gemm_kernel<C, kEpi, kWriteX, true>), dim3(static_cast<unsigned>(grid)),
-                           dim3(C::kThreads), 0, st, a, w1, w2, offs, probs, out, x_out, tokens, k_dim, n_dim, experts,
-                           limit, n_tiles, n_blocks);
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0, st, a, w1, w2, offs, probs,
+                           out, x_out, tokens, k_dim, n_dim, experts, limit, n_tiles, n_blocks);
+    };
+    if (loop == kBufLoop)
+        go(grouped_gemm_kernel<C, kEpi, kWriteX, kBufLoop>);
+    else if (loop == kBufTail)
+        go(grouped_gemm_kernel<C, kEpi, kWriteX, kBufTail>);
     else
-        hipLaunchKernelGGL((grouped_gemm_kernel<C, kEpi, kWriteX, false>), dim3(static_cast<unsigned>(grid)),
-                           dim3(C::kThreads), 0, st, a, w1, w2, offs, probs, out, x_out, tokens, k_dim, n_dim, experts,
-                           limit, n_tiles, n_blocks);
+        go(grouped_gemm_kernel<C, kEpi, kWriteX, kPtrLoop>);
 }
 
 template <class C, Epi kEpi>
@@ -736,13 +782,13 @@ int launch_grouped(const uint16_t* a, const uint16_t* w1, const uint16_t* w2, co
     const int64_t grid = grouped_grid(tokens, n_dim, kEpi == Epi::kSwiglu ? C::BN : 2 * C::BN, experts, C::BM, &n_tiles,
                                          &n_blocks);
     if (grid == 0) return MOE_EPI_ERR_BAD_SHAPE;
-    const bool buf = k_dim <= kBufMaxK<C>;
+    const int loop = k_dim > kBufMaxK<C> ? kPtrLoop : k_dim % C::BK == 0 ? kBufLoop : kBufTail;
     (void)hipGetLastError();
     if (kEpi == Epi::kSwiglu && x_out)
-        launch_kernel<C, kEpi, true>(buf, grid, st, a, w1, w2, offs, probs, out, x_out, tokens, k_dim, n_dim, experts,
+        launch_kernel<C, kEpi, true>(loop, grid, st, a, w1, w2, offs, probs, out, x_out, tokens, k_dim, n_dim, experts,
                                      limit, n_tiles, n_blocks);
     else
-        launch_kernel<C, kEpi, false>(buf, grid, st, a, w1, w2, offs, probs, out, x_out, tokens, k_dim, n_dim, experts,
+        launch_kernel<C, kEpi, false>(loop, grid, st, a, w1, w2, offs, probs, out, x_out, tokens, k_dim, n_dim, experts,
                                       limit, n_tiles, n_blocks);
     return launch_status();
 }
