@@ -36,21 +36,31 @@
 // Kernel shape (the launched configurations, ProdGateUp and ProdDown below):
 //   * A block computes a 256-token x 128-column tile of gate and the same
 //     tile of up (so each output's gate and up sit in the same lane), with
-//     eight wavefronts (4 x 2) of 64 x 64 each: 2 x 2 v_mfma_f32_32x32x16_bf16
-//     tiles for gate and 2 x 2 for up, 128 fp32 accumulators per lane, two
+//     eight wavefronts (4 x 2) of 64 x 64 each: 4 x 4 v_mfma_f32_16x16x32_bf16
+//     tiles for gate and 4 x 4 for up, 128 fp32 accumulators per lane, two
 //     wavefronts per SIMD, one block per CU (128 KiB of LDS).
-//   * Operands go from global memory straight into LDS (global_load_lds_dwordx4),
-//     K steps of 64, two LDS stages: the next step's loads are in flight while
-//     this step's MFMAs run, with no registers spent on staging. Tiles are not
-//     padded (a wavefront's load fills 1 KiB contiguously); an XOR swizzle of
-//     each row's 16-byte chunks keeps the fragment reads conflict-free.
-//   * Within a K step, the next 16-wide sub-step's fragments are read from LDS
-//     while the current one's MFMAs run, one read placed after each MFMA. One
-//     barrier per K step, before the last sub-step, a bare s_barrier after
+//   * The MFMA shape: under sustained MFMA load this part is power-limited,
+//     and the 16 x 16 x 32 instruction draws less power per FLOP than the
+//     32 x 32 x 16 one. A loop of nothing but MFMAs on all CUs, two wavefronts
+//     per SIMD, held 2.0 GHz and 2020-2055 TFLOP/s with the first against
+//     1.75 GHz and 1777-1790 TFLOP/s with the second (both at about 97% of the
+//     rate their clock allows).
+//   * Operands go from global memory straight into LDS (buffer_load_dwordx4
+//     ... lds), K steps of 64, two LDS stages: the next step's loads are in
+//     flight while this step's MFMAs run, with no registers spent on staging.
+//     Tiles are not padded (a wavefront's load fills 1 KiB contiguously); an
+//     XOR swizzle of each row's 16-byte chunks keeps the fragment reads
+//     conflict-free.
+//   * A K step is two 32-wide sub-steps of 32 MFMAs each. The next sub-step's
+//     fragments are read from LDS while the current one's MFMAs run, each
+//     fragment register refilled right after the last MFMA that uses it. One
+//     barrier per K step, between its sub-steps, a bare s_barrier after
 //     explicit waits (a __syncthreads() fence would also wait for the loads
 //     still in flight); the loads of the step after next and the next step's
-//     first fragments are issued while the last sub-step's MFMAs run, one
-//     MFMA, one load, one read at a time, the loads in buffer form.
+//     first fragments are issued while the second sub-step's MFMAs run, the
+//     loads one after every fourth MFMA. The loop runs from one barrier to
+//     the next, so that the compiler counts the fragment reads in flight
+//     instead of waiting for all of them at the top of every K step.
 //   * Tiles never straddle experts: each block finds its expert and row range
 //     from offs on the device (no host copy of offs), so a grid sized for
 //     the worst case, ceil(tokens / 256) + experts row tiles, covers any split.
@@ -68,33 +78,27 @@
 //     SwiGLU or the router multiply is applied, and each output tile is staged
 //     through LDS so that global stores are 16-byte, row-contiguous accesses.
 //     The MFMAs take the weight fragment first, so a lane's accumulators hold
-//     runs of four consecutive columns of one row; one v_permlane32_swap per
-//     pair of runs gives each lane eight consecutive bf16 columns, written to
-//     LDS with one 16-byte write (the other layout needed a 2-byte write per
-//     output): the down projection 1.3-2% faster, gate_up unchanged.
-// Measured at 131072 x 7168 x 2048 with 8 experts (every configuration gives
-// bit-identical results, each output being accumulated in the same order):
-// register-staged loads with padded LDS ran at 746-918 TFLOP/s over 22 tile
-// shapes, deeper load pipelines and fragment pipelining at up to 953, the
-// same tiles with one barrier per step at 941-965, and this loop at 1040-1060
-// (MFMA busy 54% of cycles, LDS 21%, bank conflicts 0.8% of LDS cycles) with
-// an XCD-contiguous block order, 1090-1108 with the round-robin one, and
-// 1174-1202 with the last sub-step's loads interleaved between its MFMAs.
-// Variants that did not help: K steps of 32 with 3-5 stages (850-912), two
-// 128 x 128 blocks per CU (870-890), other read placements (1007-1049), a
-// branch-free unrolled loop (1022-1032), an L2 prefetch two to four steps
-// ahead (930), A tiles three stages deep (929), four wavefronts of 128-row
-// tiles (950), raised wave priority around the MFMAs (997), a ping-pong of
-// two wavefront groups alternating fragment-read and MFMA phases (885-925),
-// accumulators in AGPRs (no change), the next step's loads spread between
-// the MFMAs of the current one (982-990), register-staged loads instead of
-// direct-to-LDS ones (775-823), A tiles three stages deep (962). Timing-only
-// copies before the interleave: MFMAs, barriers and epilogue alone 1677, plus
-// the fragment reads 1475, plus loads that all hit L2 1198, as launched 1100;
-// the loads not waited for at the barrier: no change. The shader clock averages about
-// 1.58 GHz in this kernel (busy cycles per XCD over the dispatch time; 1.74
-// before the loads were interleaved: the part is power-limited here), so
-// 2.5 PFLOP/s at 2.4 GHz is about 1.65 PFLOP/s at the clock it runs at.
+//     four consecutive columns of one row; one v_permlane16_swap per pair of
+//     tiles gives each lane eight consecutive bf16 columns, written to LDS
+//     with one 16-byte write.
+// Measured at 131072 x 7168 x 2048 with 8 experts, A/B in one process on one
+// box: with 32 x 32 x 16 MFMAs (the loop above in its earlier form, four
+// 16-wide sub-steps per K step) down 3.309 ms and gate_up 6.309 ms; with
+// 16 x 16 x 32 MFMAs 3.210 and 6.109; with the loop from barrier to barrier
+// 3.121 and 6.019 (1233 and 1279 TFLOP/s). Timing-only copies of the launched
+// loop (TFLOP/s, gate_up / down): MFMAs and epilogue alone 1899 / 1698, plus
+// the barrier 1885 / 1687, plus the fragment reads 1684 / 1532, plus the loads
+// instead of the reads 1374 / 1312: the loads set the pace. Variants that did
+// not help: the A fragments of two sub-steps held, so that they are read a
+// sub-step ahead (no change), the loads one after every second MFMA (4% slower
+// on gate_up), groups of 4 and 16 row tiles (1% slower). Earlier, with the
+// 32 x 32 x 16 loop: register-staged loads with padded LDS ran at 746-918
+// TFLOP/s over 22 tile shapes; K steps of 32 with 3-5 stages (850-912), two
+// 128 x 128 blocks per CU (870-890), an L2 prefetch two to four steps ahead
+// (930), A tiles three stages deep (929-962), four wavefronts of 128-row
+// tiles (950-1144), raised wave priority around the MFMAs (997), a ping-pong
+// of two wavefront groups (885-925) and accumulators in AGPRs (no change) did
+// not help either.
 #include "epi_common.h"
 #include "grouped_map.h"
 #include "swiglu_math.h"
@@ -205,11 +209,11 @@ struct Cfg {
 // The configurations the library launches (see the kernel-shape notes at the
 // top). They differ only in the tile group: 2 row tiles for the gate_up GEMM
 // (16 column tiles at inter 2048), 32 for the down projection (28 column
-// tiles at hidden 7168), each the best of a sweep. With the launched loop and
-// epilogue, A/B in one process: gate_up 2 row tiles 6.27-6.34 ms, 4 (the
-// earlier choice) 6.31-6.41, 1 6.40, 3 6.69, 8 6.49; down 32 3.29-3.30 ms,
-// 16 3.31-3.32, 24 3.33, 48 3.34, 64 3.35. (Earlier loops: gate_up 2-4 row
-// tiles 1107 TFLOP/s, 1 1094, 16 1079; down 32 1023, 4 1011, 14 999, 7 968.)
+// tiles at hidden 7168), each the best of a sweep. With the 16 x 16 x 32 loop,
+// A/B in one process: gate_up 2 row tiles 5.99 ms against 6.05 for 4; down
+// 32 3.11 ms against 3.13 for 16. With the 32 x 32 x 16 loop: gate_up 2 row
+// tiles 6.27-6.34 ms, 4 6.31-6.41, 1 6.40, 3 6.69, 8 6.49; down 32
+// 3.29-3.30 ms, 16 3.31-3.32, 24 3.33, 48 3.34, 64 3.35.
 using ProdGateUp = Cfg<256, 128, 4, 2, 2, 2, 2, 64>;
 using ProdDown = Cfg<256, 128, 4, 2, 2, 2, 32, 64>;
 
