@@ -288,7 +288,9 @@ struct PipeLoads {
     __device__ __forceinline__ PipeLoads(const uint16_t* a_tile, const uint16_t* g_tile, const uint16_t* u_tile,
                                          int arows, int grows, int urows, int64_t ld) {
         const int lane = static_cast<int>(threadIdx.x) % 64;
-        const int wave = static_cast<int>(threadIdx.x) / 64;
+        // wave-uniform, so that each load's LDS address (M0) is formed in scalar
+        // registers: gate_up 5.86 against 5.97 ms, down 3.04 against 3.07 ms
+        const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / 64);
 #pragma unroll
         for (int i = 0; i < kA; ++i) {
             const int slot0 = i * C::kThreads + wave * 64;
@@ -448,7 +450,7 @@ __device__ __forceinline__ void mainloop_pipe(uint16_t* lds, const uint16_t* a_t
     constexpr int MI = C::MI, NI = C::NI, kMf = 2 * MI * NI;
     static_assert(C::S == 2 && C::BK == 64, "two stages of two 32-wide sub-steps");
     const int lane = static_cast<int>(threadIdx.x) % 64;
-    const int wave = static_cast<int>(threadIdx.x) / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / 64);
     const int wm = wave / C::WN, wn = wave % C::WN;
     const PipeLoads<C> ld(a_tile, g_tile, u_tile, arows, grows, urows, k_dim);
     const int64_t nk = (k_dim + C::BK - 1) / C::BK;
@@ -622,7 +624,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     const uint16_t* u_tile = w2 + (tr.expert * n_dim + (ncols2 > 0 ? col2 : col1)) * k_dim;
 
     const int lane = static_cast<int>(threadIdx.x) % 64;
-    const int wave = static_cast<int>(threadIdx.x) / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / 64);
     const int wm = wave / C::WN, wn = wave % C::WN;
 
     f32x4 acc_g[MI][NI], acc_u[MI][NI];

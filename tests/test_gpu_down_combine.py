@@ -97,12 +97,12 @@ def test_small_named_workloads(name):
 
 
 # tails: tokens not a multiple of 256 per expert; inter not a multiple of 64 (a
-# partial K step); hidden not a multiple of 256 (the block's second 128-column
+# partial K step, its valid part shorter and longer than one 32-wide sub-step); hidden not a multiple of 256 (the block's second 128-column
 # tile partial, or absent: hidden 120 and 376); one expert; many small experts
 @pytest.mark.parametrize("tokens,inter,hidden,experts,split", [
     (300, 64, 256, 3, "dirichlet"), (257, 200, 136, 4, "one_empty"), (1000, 256, 512, 1, "even"),
     (129, 96, 120, 7, "dirichlet"), (640, 1032, 376, 16, "dirichlet"), (1, 8, 8, 1, "even"),
-    (513, 2048, 264, 2, "dirichlet"),
+    (513, 2048, 264, 2, "dirichlet"), (200, 184, 264, 3, "dirichlet"), (333, 232, 136, 5, "dirichlet"),
     # many experts: more row tiles than one tile group holds, groups spanning experts
     (3000, 128, 1024, 64, "dirichlet"),
 ])

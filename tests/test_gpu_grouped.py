@@ -103,11 +103,14 @@ def test_small_named_workload():
 
 
 # tails in every dimension: tokens not a multiple of 128 per expert, hidden not a
-# multiple of 32 (a partial K step), inter not a multiple of 128 (a partial column
-# tile), a single expert, many small experts, an empty expert
+# multiple of 64 (a partial K step, its valid part shorter than, equal to and
+# longer than one 32-wide sub-step, loaded in the prologue or inside the loop),
+# inter not a multiple of 128 (a partial column tile), a single expert, many
+# small experts, an empty expert
 @pytest.mark.parametrize("tokens,hidden,inter,experts,split", [
     (300, 64, 128, 3, "dirichlet"), (257, 200, 136, 4, "one_empty"), (1000, 512, 256, 1, "even"),
     (129, 96, 8, 7, "dirichlet"), (640, 1032, 264, 16, "dirichlet"), (1, 8, 8, 1, "even"),
+    (200, 184, 72, 3, "dirichlet"), (333, 232, 40, 5, "dirichlet"),
     # many experts: dozens of partial row tiles, the grid's tile groups span experts
     (3000, 128, 512, 64, "dirichlet"),
 ])
