@@ -58,7 +58,10 @@
 //     explicit waits (a __syncthreads() fence would also wait for the loads
 //     still in flight); the loads of the step after next and the next step's
 //     first fragments are issued while the second sub-step's MFMAs run, the
-//     loads one after every fourth MFMA. The loop runs from one barrier to
+//     loads by one wavefront per SIMD, one after every second MFMA (the other
+//     wavefront on the SIMD then never waits at a load's issue); the wave
+//     index is made uniform, so each load's LDS address (M0) is formed in
+//     scalar registers. The loop runs from one barrier to
 //     the next, so that the compiler counts the fragment reads in flight
 //     instead of waiting for all of them at the top of every K step.
 //   * Tiles never straddle experts: each block finds its expert and row range
@@ -85,13 +88,18 @@
 // box: with 32 x 32 x 16 MFMAs (the loop above in its earlier form, four
 // 16-wide sub-steps per K step) down 3.309 ms and gate_up 6.309 ms; with
 // 16 x 16 x 32 MFMAs 3.210 and 6.109; with the loop from barrier to barrier
-// 3.121 and 6.019 (1233 and 1279 TFLOP/s). Timing-only copies of the launched
+// 3.121 and 6.019 (1233 and 1279 TFLOP/s); with M0 from scalar registers 3.04
+// and 5.86 ms on another box; with one loading wavefront per SIMD 0.2-1.5%
+// faster again (three boxes). Timing-only copies of the earlier
 // loop (TFLOP/s, gate_up / down): MFMAs and epilogue alone 1899 / 1698, plus
 // the barrier 1885 / 1687, plus the fragment reads 1684 / 1532, plus the loads
 // instead of the reads 1374 / 1312: the loads set the pace. Variants that did
 // not help: the A fragments of two sub-steps held, so that they are read a
-// sub-step ahead (no change), the loads one after every second MFMA (4% slower
-// on gate_up), groups of 4 and 16 row tiles (1% slower). Earlier, with the
+// sub-step ahead (no change), all eight wavefronts loading one after every
+// second MFMA (4% slower on gate_up), half of the loads moved into the next
+// sub-step (4-6% slower), two loading wavefronts (4% slower), groups of 4
+// and 16 row tiles (1% slower), each XCD given a contiguous range of tiles
+// (7-20% slower). Earlier, with the
 // 32 x 32 x 16 loop: register-staged loads with padded LDS ran at 746-918
 // TFLOP/s over 22 tile shapes; K steps of 32 with 3-5 stages (850-912), two
 // 128 x 128 blocks per CU (870-890), an L2 prefetch two to four steps ahead
@@ -195,12 +203,17 @@ struct Cfg {
     static constexpr int kWElems = BN * BK;
     static constexpr int kStageElems = kAElems + 2 * kWElems;
     static constexpr int kLdo = BN + 8;
-    static constexpr int kAChunks = BM * BK / 8 / kThreads;
-    static constexpr int kWChunks = BN * BK / 8 / kThreads;
+    // The global -> LDS loads are issued by four of the eight wavefronts (one
+    // per SIMD), so that the other wavefront on each SIMD never waits at a
+    // load's issue and keeps the MFMA unit fed: 0.2-1.5% faster than all eight
+    // loading (three boxes), two loading wavefronts 4% slower.
+    static constexpr int kLoadWaves = 4, kLoadThreads = 64 * kLoadWaves;
+    static constexpr int kAChunks = BM * BK / 8 / kLoadThreads;
+    static constexpr int kWChunks = BN * BK / 8 / kLoadThreads;
     static constexpr int kLdsElems = S * kStageElems > BM * kLdo ? S * kStageElems : BM * kLdo;
     static_assert(MI >= 1 && NI >= 2 && NI % 2 == 0 && BM % (16 * WM) == 0 && BN % (16 * WN) == 0,
                   "whole MFMA tiles, pairs of column tiles for the epilogue's exchange");
-    static_assert(kAChunks >= 1 && kWChunks >= 1 && BM * BK % (8 * kThreads) == 0 && BN * BK % (8 * kThreads) == 0,
+    static_assert(kAChunks >= 1 && kWChunks >= 1 && BM * BK % (8 * kLoadThreads) == 0 && BN * BK % (8 * kLoadThreads) == 0,
                   "whole 16-byte chunks per thread");
     static_assert(S == 2, "two LDS stages");
     static_assert(BM * BN % (8 * kThreads) == 0, "whole output chunks per thread");
@@ -293,7 +306,7 @@ struct PipeLoads {
         const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / 64);
 #pragma unroll
         for (int i = 0; i < kA; ++i) {
-            const int slot0 = i * C::kThreads + wave * 64;
+            const int slot0 = i * C::kLoadThreads + (wave % C::kLoadWaves) * 64;
             const int row = (slot0 + lane) / C::kCpr;
             const int kq = ((slot0 + lane) % C::kCpr) ^ swz<C::kCpr>(row);
             oa[i] = slot0;
@@ -302,7 +315,7 @@ struct PipeLoads {
         }
 #pragma unroll
         for (int i = 0; i < kW; ++i) {
-            const int slot0 = i * C::kThreads + wave * 64;
+            const int slot0 = i * C::kLoadThreads + (wave % C::kLoadWaves) * 64;
             const int row = (slot0 + lane) / C::kCpr;
             const int kq = ((slot0 + lane) % C::kCpr) ^ swz<C::kCpr>(row);
             ow[i] = slot0;
@@ -377,13 +390,13 @@ struct PipeLoads {
         uint16_t* dst;
         int slot0;
         if (i < kA) {
-            slot0 = i * C::kThreads + wave * 64;
+            slot0 = i * C::kLoadThreads + (wave % C::kLoadWaves) * 64;
             tile = a_tile;
             voff = b.va[i];
             dst = st + slot0 * 8;
         } else {
             const int j = (i - kA) / 2;
-            slot0 = j * C::kThreads + wave * 64;
+            slot0 = j * C::kLoadThreads + (wave % C::kLoadWaves) * 64;
             const bool up = (i - kA) % 2 == 1;
             tile = up ? u_tile : g_tile;
             voff = up ? b.vu[j] : b.vg[j];
@@ -400,6 +413,7 @@ struct PipeLoads {
 
     // Loads of K step kt into `st` (one stage of LDS).
     __device__ __forceinline__ void issue(uint16_t* st, int64_t kt, int64_t k_dim) const {
+        if (__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / 64) >= C::kLoadWaves) return;
         const int lane = static_cast<int>(threadIdx.x) % 64;
         const int64_t k0 = kt * C::BK;
         uint16_t* sa = st;
@@ -521,9 +535,9 @@ __device__ __forceinline__ void mainloop_pipe(uint16_t* lds, const uint16_t* a_t
         // The loop runs from the middle of one K step to the middle of the
         // next, so that its head follows a barrier (where every read has been
         // waited for) and the waits between sub-steps are counted exactly.
-        // Sub-step 1 of step kt issues the loads of step kt + 2, one after
-        // every kEvery-th MFMA, between the reads of step kt + 1's first
-        // fragments: in buffer form while that step is a full K step, in
+        // Sub-step 1 of step kt issues the loads of step kt + 2 (in the loading
+        // wavefronts), one after every kEvery-th MFMA, between the reads of
+        // step kt + 1's first fragments: in buffer form while that step is a full K step, in
         // pointer form with zeros past K for the step that crosses the end of
         // K (uniform branches). Issued together before the MFMAs, the loads held
         // the wavefronts at issue while the MFMA units idled (1072 against 1174
@@ -545,7 +559,7 @@ __device__ __forceinline__ void mainloop_pipe(uint16_t* lds, const uint16_t* a_t
 #pragma unroll
             for (int i = 0; i < kMf; ++i) {
                 mfma(i);
-                if (i % kEvery == 0 && i / kEvery < kLoads) {
+                if (i % kEvery == 0 && i / kEvery < kLoads && wave < C::kLoadWaves) {
                     if (kn < nfull) {
                         ld.issue_one(bufs, cur, kn, i / kEvery);
                     } else if constexpr (kLoop == kBufTail) {
