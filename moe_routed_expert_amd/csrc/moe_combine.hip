@@ -14,35 +14,59 @@
 // Every element of out gets the same sequence of binary32 operations as this
 // definition, so the result is bit-exact whatever the launch shape.
 //
-// Shape: one block per token (a grid-stride loop past kMaxBlocks tokens), B
-// lanes that own V quads (4 consecutive elements) each per pass over the row,
-// B * V about the row's quad count (hidden 7168: B = 896, V = 2, one pass). The
-// token's slot indices are block-uniform, read 8 at a time with unrolled scalar
-// loads (a loop that reads one index per iteration was compiled to vector
-// loads, each waited for in turn: 65% of peak instead of 73%), so each routed
-// row's base address lives in scalar registers. Rows are taken kRows at
-// a time: the loads of up to kRows rows are all issued before their adds
-// (which then run in slot order), so a token with several local rows waits
-// for one memory latency, not one per row. A wavefront's quad access covers
-// 1 KiB of float32 or 512 bytes of 16-bit data contiguously. Rows and output
-// are streamed once: nontemporal accesses.
+// Shape: a token's row is cut into segments of kSegQuads quads (4 consecutive
+// elements each; 1024 elements, 4 KiB of float32), one 128-lane block per
+// (token, segment) pair, each lane two quads of the segment 128 quads apart,
+// so every wavefront-wide quad access covers one contiguous 1 KiB (float32)
+// or 512 bytes (16-bit) run. A grid-stride loop takes the pairs past
+// kMaxBlocks. The token's slot indices are block-uniform, read 8 at a time
+// with unrolled scalar loads, so each routed row's base address lives in
+// scalar registers; the local slots of a chunk are kept as a bit mask and
+// taken in ascending order, up to kRows rows at a time, whose loads are all
+// issued before their adds (which then run in slot order): a token with
+// several local rows waits for one memory latency, not one per row. No
+// private array is indexed at run time: one that was (a compacted list of the
+// chunk's rows) was placed in LDS by the compiler, 8 bytes per lane for each
+// of the 1024 lanes the launch bounds allowed, 64 KiB per block. Rows and
+// output are streamed once: nontemporal accesses.
 //
-// Measured at 131072 tokens x 7168 float32 (top-8 of 64 experts, 8 local):
-// one row at a time with 256 lanes x 7 quads ran at 65-67% of HBM peak; three
-// rows at a time 70-71%; with 896 lanes x 2 quads 73%. Limiting the resident
-// blocks (by LDS, to 2-8 per CU) changed nothing; a persistent grid with the
-// next token's slots prefetched, and a wavefront per token, ran at 62-69%. The
-// same kernel on an identity routing (one row per token, in order) ran no
-// faster, so the gather itself costs nothing measurable.
+// Residency. With float32 rows the kernel reads and writes equal byte
+// counts, and HBM served that mix fastest with about 24 wavefronts per CU in
+// flight: each block reserves kCapLds bytes of LDS that it never touches, so
+// that at most kBlocksPerCu blocks share a CU's 160 KiB. With 16-bit rows
+// (two thirds of the bytes are writes) the cap made it slower, and a CU holds
+// as many blocks as its wavefront slots allow.
+//
+// Measured at 131072 tokens x 7168 float32 (top-8 of 64 experts, 8 local),
+// launched back to back: 1196-1202 us, 78.2-78.6% of HBM peak (one block per
+// token: 1277-1301 us, 72.2-73.3%). With a 1 GiB write before every launch,
+// bit-identical outputs, in one process per row below: one 896-lane
+// block per token (two quads per lane) 73.1-73.6% of HBM peak; 128-lane
+// segments with 16 blocks per CU 76.5-76.8%, 14 80.9%, 13 82.6%, 12
+// 82.1-82.4%, 11 79.1%, 10 78.7%, 8 74.8%; 64- and 192-lane segments
+// 76.6-82.7% and 80.2-81.7% by residency; 256- and 448-lane segments with
+// one quad per lane 70.2% and 58.2%; XCD granules of 16 or 64 blocks 65.5%
+// and 74.0%. With 16-bit rows: 65.2% one block per token, 69.3% in 128-lane
+// segments uncapped, 52.5% capped at 12. At 32768 x 16384 float32: 71.9%
+// one block per token, 82.3% in segments. Earlier variants of the one block
+// per token shape: one row at a time with 256 lanes x 7 quads 65-67%, a
+// persistent grid with the next token's slots prefetched, and a wavefront per
+// token, 62-69%; the same kernel on an identity routing (one row per token, in
+// order) ran no faster, so the gather itself costs nothing measurable.
 #include "epi_common.h"
 
 namespace moe_epi {
 namespace {
 
-constexpr int kMaxThreads = 1024;
-constexpr int kRows = 3;       // routed rows whose loads are in flight together
-constexpr int kSlotChunk = 8;  // slot indices read (unrolled scalar loads) per round
+constexpr int kLanes = 128;        // lanes per block
+constexpr int kQuadsPerLane = 2;   // quads of the segment per lane, kLanes apart
+constexpr uint32_t kSegQuads = kLanes * kQuadsPerLane;
+constexpr int kRows = 4;           // routed rows whose loads are in flight together
+constexpr int kSlotChunk = 8;      // slot indices read (unrolled scalar loads) per round
 constexpr int64_t kMaxTopK = 1024;  // slots per token accepted (the pages route to a handful)
+constexpr int kLdsPerCu = 160 * 1024;  // gfx950
+constexpr int kBlocksPerCu = 12;       // float32 rows: resident blocks per CU
+constexpr int kCapLds = kLdsPerCu / kBlocksPerCu / 256 * 256;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -58,77 +82,83 @@ __device__ __forceinline__ f32x4 load_quad(const void* row, uint32_t e) {
     }
 }
 
-template <int T, int V>
-__global__ __launch_bounds__(kMaxThreads) void moe_combine_kernel(const void* __restrict__ expert_out,
-                                                                  const int32_t* __restrict__ row_of,
-                                                                  float* __restrict__ out, int64_t rows,
-                                                                  int64_t tokens, int64_t top_k, int64_t hidden) {
+template <int T>
+__global__ __launch_bounds__(kLanes) void moe_combine_kernel(const void* __restrict__ expert_out,
+                                                             const int32_t* __restrict__ row_of,
+                                                             float* __restrict__ out, int64_t rows, int64_t tokens,
+                                                             int64_t top_k, int64_t hidden, uint32_t nseg) {
     const uint32_t nq = static_cast<uint32_t>(hidden / 4);
-    const uint32_t lane = threadIdx.x, nb = blockDim.x;
-    for (int64_t t = blockIdx.x; t < tokens; t += gridDim.x) {
+    const int64_t pairs = tokens * static_cast<int64_t>(nseg);
+    for (int64_t b = blockIdx.x; b < pairs; b += gridDim.x) {
+        const int64_t t = b / nseg;
+        const uint32_t c0 = static_cast<uint32_t>(b - t * nseg) * kSegQuads + threadIdx.x;
         const int32_t* slots = row_of + t * top_k;
-        float* orow = out + t * hidden;
-        for (uint32_t c0 = lane; c0 < nq; c0 += nb * V) {
-            f32x4 acc[V];
+        f32x4 acc[kQuadsPerLane];
 #pragma unroll
-            for (int k = 0; k < V; ++k) acc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            for (int64_t j0 = 0; j0 < top_k; j0 += kSlotChunk) {
-                // the chunk's local rows, in slot order (block-uniform: scalar loads and registers)
-                int64_t list[kSlotChunk];
+        for (int k = 0; k < kQuadsPerLane; ++k) acc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int64_t j0 = 0; j0 < top_k; j0 += kSlotChunk) {
+            // the chunk's rows (block-uniform: scalar loads and registers), local ones flagged in `mask`
+            int64_t r[kSlotChunk];
+            uint32_t mask = 0;
+#pragma unroll
+            for (int jj = 0; jj < kSlotChunk; ++jj) {
+                r[jj] = -1;
+                if (j0 + jj < top_k) {
+                    r[jj] = __builtin_amdgcn_readfirstlane(slots[j0 + jj]);
+                    if (r[jj] >= 0 && r[jj] < rows) mask |= 1u << jj;
+                }
+            }
+            while (mask) {
+                int64_t rr[kRows];
                 int n = 0;
 #pragma unroll
-                for (int jj = 0; jj < kSlotChunk; ++jj) {
-                    if (j0 + jj < top_k) {
-                        const int64_t r = __builtin_amdgcn_readfirstlane(slots[j0 + jj]);
-                        if (r >= 0 && r < rows) list[n++] = r;
+                for (int q = 0; q < kRows; ++q) {
+                    rr[q] = 0;
+                    if (mask) {  // the lowest flagged slot, picked by compile-time indices only
+                        const int j = __builtin_ctz(mask);
+                        mask &= mask - 1;
+                        int64_t v = r[0];
+#pragma unroll
+                        for (int jj = 1; jj < kSlotChunk; ++jj)
+                            if (j == jj) v = r[jj];
+                        rr[q] = v;
+                        n = q + 1;
                     }
                 }
-                for (int i = 0; i < n; i += kRows) {
-                    f32x4 v[kRows][V];
+                f32x4 v[kRows][kQuadsPerLane];
 #pragma unroll
-                    for (int q = 0; q < kRows; ++q) {
-                        if (i + q >= n) continue;
-                        const void* erow = row_at<T>(expert_out, list[i + q] * hidden);
+                for (int q = 0; q < kRows; ++q) {
+                    if (q >= n) continue;
+                    const void* erow = row_at<T>(expert_out, rr[q] * hidden);
 #pragma unroll
-                        for (int k = 0; k < V; ++k) {
-                            const uint32_t c = c0 + k * nb;
-                            v[q][k] = c < nq ? load_quad<T>(erow, 4 * c) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                        }
+                    for (int k = 0; k < kQuadsPerLane; ++k) {
+                        const uint32_t c = c0 + k * kLanes;
+                        v[q][k] = c < nq ? load_quad<T>(erow, 4 * c) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                     }
-#pragma unroll
-                    for (int q = 0; q < kRows; ++q)
-                        if (i + q < n)
-#pragma unroll
-                            for (int k = 0; k < V; ++k) acc[k] = acc[k] + v[q][k];
                 }
-            }
 #pragma unroll
-            for (int k = 0; k < V; ++k) {
-                const uint32_t c = c0 + k * nb;
-                if (c < nq) store_nt16(at<4>(orow, 4 * c), __builtin_bit_cast(u32x4, acc[k]));
+                for (int q = 0; q < kRows; ++q)
+                    if (q < n)
+#pragma unroll
+                        for (int k = 0; k < kQuadsPerLane; ++k) acc[k] = acc[k] + v[q][k];
             }
+        }
+        float* orow = out + t * hidden;
+#pragma unroll
+        for (int k = 0; k < kQuadsPerLane; ++k) {
+            const uint32_t c = c0 + k * kLanes;
+            if (c < nq) store_nt16(at<4>(orow, 4 * c), __builtin_bit_cast(u32x4, acc[k]));
         }
     }
 }
 
-// Quads per lane and lanes per block for a row of nq quads: V = 1, 2 or 4 and
-// B a multiple of 64 with B * V >= nq where that fits in one block, else
-// kMaxThreads x 4 and several passes.
 template <int T>
 void launch_combine(const void* eo, const int32_t* row_of, float* out, int64_t rows, int64_t tokens, int64_t top_k,
                     int64_t hidden, hipStream_t st) {
-    const int64_t nq = hidden / 4;
-    const int v = nq <= kMaxThreads ? 1 : (nq <= 2 * kMaxThreads ? 2 : 4);
-    int64_t b = (nq + v - 1) / v;
-    b = (b + 63) / 64 * 64;
-    if (b > kMaxThreads) b = kMaxThreads;
-    const dim3 grid(grid_for_rows(tokens, 1)), block(static_cast<unsigned>(b));
-    if (v == 1)
-        hipLaunchKernelGGL((moe_combine_kernel<T, 1>), grid, block, 0, st, eo, row_of, out, rows, tokens, top_k, hidden);
-    else if (v == 2)
-        hipLaunchKernelGGL((moe_combine_kernel<T, 2>), grid, block, 0, st, eo, row_of, out, rows, tokens, top_k, hidden);
-    else
-        hipLaunchKernelGGL((moe_combine_kernel<T, 4>), grid, block, 0, st, eo, row_of, out, rows, tokens, top_k, hidden);
+    const int64_t nseg = (hidden / 4 + kSegQuads - 1) / kSegQuads;
+    const int lds = T == MOE_EPI_F32 ? kCapLds : 0;
+    hipLaunchKernelGGL((moe_combine_kernel<T>), dim3(grid_for_rows(tokens * nseg, 1)), dim3(kLanes), lds, st, eo,
+                       row_of, out, rows, tokens, top_k, hidden, static_cast<uint32_t>(nseg));
 }
 
 }  // namespace

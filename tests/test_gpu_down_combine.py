@@ -209,11 +209,14 @@ def test_combine_small_named_workload():
     check_combine(d["expert_out"], EO_CODE[w.eo_dtype], d["row_of"], d["rows"], w.hidden, w.name)
 
 
-# hidden: one quad per lane or fewer (8, 520), several (1032: two, 7168: seven),
-# more than one pass over the row (8200: nine quads per lane, capped at eight)
+# hidden against the 1024-element row segments a block takes: one partial segment (8, 520),
+# a full one and two elements (1032), seven full ones (7168), eight and a partial ninth (8200).
+# top_k: one slot, chunks of eight slot indices with more local rows than are loaded at once
+# (12 of 16 experts, all local), and the largest top_k accepted.
 @pytest.mark.parametrize("eo_dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("tokens,hidden,top_k,ge,le", [
     (777, 1032, 8, 64, 8), (300, 8, 2, 8, 4), (513, 520, 4, 16, 16), (64, 8200, 6, 32, 32), (1, 7168, 1, 4, 2),
+    (200, 1032, 12, 16, 16), (3, 64, 1024, 1024, 512),
 ])
 def test_combine_shapes_and_dtypes(eo_dtype, tokens, hidden, top_k, ge, le):
     w = CombineWorkload(f"c_{tokens}x{hidden}_k{top_k}_e{ge}of{le}_{eo_dtype}", tokens, hidden, top_k, ge, le,
@@ -380,6 +383,8 @@ def test_down_with_more_than_2_31_output_elements():
 
 
 def test_combine_with_more_than_2_31_elements():
+    """Past 2^31 elements, and with 300000 x 7 (token, segment) pairs more than the grid
+    holds, so blocks take several pairs each."""
     tokens, hidden, top_k = 300000, 7168, 2
     rows = 320000
     g = torch.Generator(device="cuda").manual_seed(54)
