@@ -138,7 +138,7 @@ def test_every_token_in_one_expert_of_sixteen():
     check(d, 2000, 96, 256, 16, 7.0, "one expert holds every token")
 
 
-def test_full_size_sampled_rows():
+def test_full_size_sampled_rows_and_every_epilogue_row():
     w = GROUPED_WORKLOADS["grouped_131072x7168x2048_e8"]
     say(f"{w.name}: generate")
     d = w.generate()
@@ -164,9 +164,11 @@ def test_full_size_sampled_rows():
     s, s_abs = oracle.grouped_gate_up(d["a"][idx], d["w_gate"], d["w_up"], sub_offs, idx.size, w.hidden, w.inter,
                                       w.experts, with_abs_sum=True)
     sx = assert_gemm_bf16_within(x[idx], s, s_abs, w.hidden, f"{w.name} x")
-    y_o = oracle.swiglu_clamped_fwd(x[idx], d["probs"][idx], idx.size, w.inter, w.limit)
-    sy = assert_bf16_parity(y[idx], y_o, f"{w.name} y")
-    say(f"{w.name}: x {sx}, y exact {sy['exact']:.5f}")
+    # the epilogue on every row: the oracle's SwiGLU forward of the kernel's own x
+    say(f"{w.name}: oracle epilogue on every row")
+    y_o = oracle.swiglu_clamped_fwd(x, d["probs"], w.tokens, w.inter, w.limit)
+    sy = assert_bf16_parity(y, y_o, f"{w.name} y")
+    say(f"{w.name}: x {sx} on {idx.size} sampled rows, y exact {sy['exact']:.5f} on all {w.tokens}")
 
 
 @pytest.mark.parametrize("k_dim", [4177920, 4178048])
