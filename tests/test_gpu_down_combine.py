@@ -168,6 +168,24 @@ def test_down_full_size_sampled_rows(name):
     say(f"{w.name}: {st}")
 
 
+def test_down_full_size_bf16_output_is_the_rounded_fp32_output_everywhere():
+    """Every element at full size: both epilogues multiply the same bf16 rounding of the
+    same accumulator by p in fp32, so the bf16 output must be the bf16 rounding (to
+    nearest, ties to even) of the fp32 output. The sampled rows above tie the fp32
+    output to the oracle."""
+    w = DOWN_WORKLOADS["down_131072x2048x7168_e8"]
+    say(f"{w.name}: generate")
+    d = w.generate()
+    say(f"{w.name}: gpu, fp32 and bf16 outputs")
+    o32 = run_down(d, w.tokens, w.hidden, True)
+    o16 = run_down(d, w.tokens, w.hidden, False)
+    assert not (o32.view(torch.int32) == SENTINEL32).any().item(), f"{w.name}: fp32 rows left unwritten"
+    same = torch.equal(o32.to(torch.bfloat16).view(torch.int16), o16.view(torch.int16))
+    torch.cuda.synchronize()
+    assert same, f"{w.name}: bf16 output differs from the rounded fp32 output"
+    say(f"{w.name}: bf16 output == bf16(fp32 output) on all {w.tokens} x {w.hidden}")
+
+
 # ---- combine ------------------------------------------------------------------------
 
 EO_TORCH = {oracle.BF16: torch.bfloat16, oracle.F16: torch.float16, oracle.F32: torch.float32}
