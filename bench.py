@@ -25,12 +25,12 @@ Prints one JSON line. Options:
   --no-grad-probs    backward without the probability gradient (probabilities
                      that carry no gradient; the router then does not read x)
   --no-cpu-baseline  skip the oracle timing on the host
-  --warm             SwiGLU / router: launch each kernel straight after the
-                     previous one. The default is a 1 GiB write before every
-                     launch, outside its events, which evicts L2 and the 256 MB
-                     Infinity Cache, so a workload smaller than them is not
-                     served from them; the step time is then the sum of the
-                     two kernels' event times
+  --warm             SwiGLU / router / combine: launch each kernel straight
+                     after the previous one. The default is a 1 GiB write
+                     before every launch, outside its events, which evicts L2
+                     and the 256 MB Infinity Cache, so a workload smaller than
+                     them is not served from them; the step time is then the
+                     sum of the kernels' event times
   --no-copy-ceiling  skip timing the 1 GiB device copy whose bandwidth the
                      SwiGLU / router lines also report a fraction of (it runs
                      after the host-side input generation, before the
@@ -101,7 +101,7 @@ def parse_args():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-x", action="store_true")
     ap.add_argument("--warm", action="store_true",
-                    help="SwiGLU / router: no cache flush between launches (default: a 1 GiB write before each)")
+                    help="SwiGLU / router / combine: no cache flush between launches (default: a 1 GiB write before each)")
     ap.add_argument("--no-copy-ceiling", action="store_true",
                     help="SwiGLU / router: do not time the 1 GiB device copy (the box's copy ceiling)")
     ap.add_argument("--settle-seconds", type=float, default=0.1,
@@ -709,6 +709,28 @@ def time_launches(step, args):
     return np.array([e0.elapsed_time(e1) for e0, e1 in evs]), wall * 1e3 / args.steps
 
 
+def time_flushed(launch, args, dev):
+    """Warm up, then time args.steps launches, each after a 1 GiB write (a fill
+    kernel, outside the launch's events): per-launch ms from HIP events."""
+    import numpy as np
+    import torch
+    scratch = torch.empty((1 << 28,), dtype=torch.float32, device=dev)
+    print(f"[bench] warmup {args.warmup} steps (caches flushed before every launch)", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        scratch.zero_()
+        launch()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    for e0, e1 in evs:
+        scratch.zero_()
+        e0.record()
+        launch()
+        e1.record()
+    torch.cuda.synchronize()
+    return np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+
+
 def oracle_timed(run, seconds):
     """Whole passes of run() until `seconds` are spent (at least one, at most 100): (passes, s)."""
     passes, t = 0, time.perf_counter()
@@ -813,7 +835,12 @@ def combine_main(args, w):
             torch.bfloat16 if w.eo_dtype == "bf16" else torch.float16).to(dev)
     ro = torch.from_numpy(row_of).to(dev)
     out = torch.empty((w.tokens, w.hidden), dtype=torch.float32, device=dev)
-    ms, ms_per_step = time_launches(lambda: epi.moe_combine_fwd(eo, ro, out), args)
+    launch = lambda: epi.moe_combine_fwd(eo, ro, out)
+    if args.warm:
+        ms, ms_per_step = time_launches(launch, args)
+    else:  # as the SwiGLU lines: a 1 GiB write before every launch, outside its events
+        ms = time_flushed(launch, args, dev)
+        ms_per_step = float(ms.mean())
     nbytes = w.min_bytes(row_of, rows)
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     avg_ms = float(ms.mean())
@@ -866,7 +893,9 @@ def combine_main(args, w):
         "config": {"workload": w.name, "op": "combine", "tokens": w.tokens, "hidden": w.hidden, "top_k": w.top_k,
                    "global_experts": w.global_experts, "local_experts": w.local_experts, "rows": rows,
                    "expert_out": w.eo_dtype, "io": f"{w.eo_dtype} routed rows, int32 row_of, fp32 out; fp32 adds",
-                   "bytes_per_step": nbytes},
+                   "bytes_per_step": nbytes,
+                   "caches": "warm from the previous launch" if args.warm else
+                   "flushed before every launch (1 GiB write outside the events)"},
         "frac_of_peak": value / PEAK_HBM_GBS,
         "kernels": kernels,
         "roofline": roofline,
