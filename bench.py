@@ -588,6 +588,17 @@ def epilogue_main(args, w):
     }
     if cpu1 is not None:
         line["cpu_baseline_1thread"] = cpu1
+    if headline and w.op == "swiglu":
+        # The pages' one timing, on other hardware and another implementation:
+        # context for the backward, never vs_baseline.
+        line["context"] = {
+            "source": "page nemo_automodel.components.moe.swiglu_triton, module description",
+            "figure": "a torch.compile backward of this op (d_gate and d_up concatenated) on GB200: "
+                      "about 0.7 ms over about 1.1 GB at the large-node shape, near one quarter of that "
+                      "GPU's HBM bandwidth",
+            "this_run_backward_ms": kernels[names[1]]["avg_us"] / 1e3,
+            "this_run_backward_bytes": bwd_b,
+        }
     print(json.dumps(line), flush=True)
 
 
